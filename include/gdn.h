@@ -1,0 +1,189 @@
+/*
+ * gdn.h -- libgdn: the Gated DeltaNet (GDN) recurrence of a speculative-decoding
+ * verify pass, its GPU-resident commit, and its chunked prefill, for AMD MI355X
+ * (gfx950).  Plain C ABI: device pointers, sizes and a HIP stream; no framework
+ * types.
+ *
+ * The recurrence.  The lithos-metal README ("How it works", region table, "GDN
+ * mixer" row) partitions a GDN layer's recurrent state by value columns and keeps
+ * each slice on chip across a block of input tokens; the devdoido audit ("How does
+ * lithos-metal fuse layer mixers on Metal?") says the state is fp32 with a key side
+ * and a value side.  The update is the gated delta rule of Gated DeltaNet (Yang,
+ * Kautz & Hatamizadeh, ICLR 2025), per (instance, head):
+ *
+ *     S_t = a_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,    o_t = S_t q_t
+ *
+ * with S in R^{dv x dk} (row i = value index i), a_t = exp(g_t) where g is the
+ * log-decay, and no scaling of q inside the library.
+ *
+ * Layouts (row-major; every buffer is a caller-owned device allocation):
+ *     S          fp32  [B][H][dv][dk]
+ *     q, k       in_dt [B][T][H][dk]      (T = block rows, or L = prompt length)
+ *     v          in_dt [B][T][H][dv]
+ *     g, beta    fp32  [B][T][H]
+ *     o          fp32  [B][T][H][dv]
+ * B counts independent instances (GDN layers or sequences), H heads per instance.
+ *
+ * Conventions shared by every call:
+ *   - Calls validate their host-visible arguments first and return a negative
+ *     gdn_status without launching anything when one is bad.
+ *   - Calls enqueue their kernels on `hip_stream` (a hipStream_t; NULL means the
+ *     null stream) and return without synchronising the host, except
+ *     gdn_record_status, which is a synchronising diagnostic.
+ *   - The library allocates no device memory and keeps no global state; all
+ *     scratch is in caller-provided buffers.
+ *   - Device pointers must be 16-byte aligned (g, beta, n_accepted, pos: 4-byte).
+ *   - NaN or Inf inputs propagate to outputs; nothing on the hot path checks them.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct gdn_shape {
+    int32_t B;   /* independent instances, >= 1 */
+    int32_t H;   /* heads per instance, >= 1 */
+    int32_t dk;  /* key head dimension: 64 or 128 */
+    int32_t dv;  /* value head dimension: 64 or 128 */
+} gdn_shape;
+
+typedef enum gdn_in_dtype {
+    GDN_IN_F32 = 0,   /* q, k, v are fp32 */
+    GDN_IN_BF16 = 1   /* q, k, v are bf16 (the library never rounds them) */
+} gdn_in_dtype;
+
+typedef enum gdn_status {
+    GDN_OK = 0,
+    GDN_EINVAL = -1,  /* null or misaligned pointer, unknown dtype */
+    GDN_EDIM = -2,    /* B or H < 1, dk or dv not in {64, 128}, sizes overflow */
+    GDN_ERANGE = -3,  /* T not in [1, 16], L < 0, chunk not 64 */
+    GDN_EWS = -4,     /* record or workspace smaller than required */
+    GDN_EHIP = -5     /* the HIP runtime reported an error */
+} gdn_status;
+
+/* Error bits a commit leaves in the block record (read by gdn_record_status). */
+enum {
+    GDN_REC_NO_BLOCK = 1,  /* no verified block to commit: never verified, or already committed */
+    GDN_REC_N_RANGE = 2,   /* n_accepted[b] outside [0, T] */
+    GDN_REC_SHAPE = 4      /* the record was written for another shape */
+};
+
+/* Largest verify block. */
+#define GDN_T_MAX 16
+/* The only chunk length the prefill supports. */
+#define GDN_PREFILL_CHUNK 64
+
+/*
+ * Bytes of the block record that gdn_verify_block writes and gdn_commit consumes,
+ * for `T` rows of shape `shp` with inputs of dtype `in_dt`.  The record holds a
+ * header, per-instance control words, the rows' log-decay prefix sums, the rows'
+ * delta vectors (fp32) and a copy of the rows' keys (in_dt).  Returns 0 for an
+ * invalid shape, T or dtype.
+ */
+size_t gdn_block_record_bytes(const gdn_shape *shp, int32_t T, gdn_in_dtype in_dt);
+
+/*
+ * Verify a speculative block: the outputs o_1..o_T of T consecutive tokens (the
+ * anchor plus T-1 drafted tokens) from the checkpoint state S, without changing S.
+ *
+ * Source: the lithos-metal README, DSpark paragraph (the target verifies the
+ * drafted block and then commits the accepted prefix) and its quick start (seven
+ * drafted tokens verified together with one anchor); the devdoido audit, "How
+ * does DSpark speculative decoding create more than one token per read?" (each
+ * token is one row, eight rows in one pass).  T = 8 is that block.
+ *
+ *   S        fp32 [B][H][dv][dk], read only: S is the block's checkpoint.
+ *   q, k, v  the block's rows, layouts above, dtype in_dt.
+ *   g, beta  fp32 [B][T][H]: log-decay (a = exp(g)) and write strength.
+ *   T        rows in the block, 1..GDN_T_MAX.
+ *   o        fp32 [B][T][H][dv], written: o_t = S_t q_t for t = 1..T.
+ *   record   device buffer of at least gdn_block_record_bytes(shp, T, in_dt)
+ *            bytes; zero-filled once by the caller after allocation, then owned
+ *            by the library's calls.  Overwritten: it becomes the pending block
+ *            that gdn_commit consumes, replacing any block not yet committed.
+ *
+ * Returns GDN_OK or a negative gdn_status (nothing launched on a bad argument).
+ */
+int gdn_verify_block(const float *S, const void *q, const void *k, const void *v,
+                     const float *g, const float *beta, int32_t T, gdn_in_dtype in_dt,
+                     const gdn_shape *shp, float *o, void *record, size_t record_bytes,
+                     void *hip_stream);
+
+/*
+ * Commit the accepted prefix of the pending block on the GPU: S <- S_n, the state
+ * after the first n = n_accepted[b] rows of the block, for each instance b.
+ *
+ * Source: the lithos-metal README, "How it works" (GPU-resident state tracks token
+ * positions, accepted tokens and recurrent-state commit/rollback with minimal CPU
+ * involvement) and its DSpark paragraph (commit of the accepted prefix); the
+ * devdoido audit, DSpark section (rewind brings the recurrent state in line with
+ * the accepted tokens after every acceptance decision).
+ *
+ *   S           fp32 [B][H][dv][dk], the same checkpoint given to the verify;
+ *               updated in place.  n = 0 leaves every byte of S untouched
+ *               (full rollback); n = T keeps the whole block.
+ *   record      the record written by the last gdn_verify_block of this shape.
+ *   n_accepted  device int32 [B]: rows of the block to keep, anchor included,
+ *               0..T.  Read on the device; the host never sees it.
+ *   pos         device int32 [B] or NULL: advanced by n on success.
+ *   shp         must equal the verify's shape (checked on the device).
+ *
+ * The pending block is consumed: a second commit without a new verify changes
+ * nothing and sets GDN_REC_NO_BLOCK.  An n outside [0, T] or a shape mismatch
+ * changes nothing for that instance and sets GDN_REC_N_RANGE / GDN_REC_SHAPE;
+ * such an instance's block stays pending.  Returns GDN_OK or a negative gdn_status.
+ */
+int gdn_commit(float *S, void *record, const int32_t *n_accepted, int32_t *pos,
+               const gdn_shape *shp, void *hip_stream);
+
+/*
+ * Diagnostic: copy each instance's commit error bits (GDN_REC_*) into
+ * host_err_bits[0..B-1].  Synchronises `hip_stream`.  Bits are cleared by the
+ * next gdn_verify_block.
+ */
+int gdn_record_status(const void *record, const gdn_shape *shp, int32_t *host_err_bits,
+                      void *hip_stream);
+
+/*
+ * Bytes of workspace gdn_prefill_chunked needs for prompt length L; 0 means the
+ * call needs none (ws may then be NULL).
+ */
+size_t gdn_prefill_workspace_bytes(const gdn_shape *shp, int32_t L, int32_t chunk);
+
+/*
+ * Chunked prefill: run the recurrence over an L-token prompt, writing every
+ * output and advancing S from the initial to the final state.
+ *
+ * Source: the devdoido audit, "What does long-context prefill cost on Apple
+ * silicon?" (prefill dominates long-context use), with the chunkwise UT/WY form of
+ * the gated delta rule (Gated DeltaNet, ICLR 2025): within a chunk the products
+ * are dense contractions, between chunks only the fp32 state is carried.
+ *
+ *   S        fp32 [B][H][dv][dk], in: initial state, out: state after L tokens.
+ *   q, k, v, g, beta, o   as for the verify, with L rows.  L >= 0 (L = 0 is a
+ *            no-op); the last chunk may be partial.
+ *   chunk    GDN_PREFILL_CHUNK.
+ *   ws       workspace of gdn_prefill_workspace_bytes(...) bytes (may be NULL
+ *            when that is 0).
+ *
+ * Splitting a prompt is exact up to rounding: prefill(L1) then prefill(L2) on the
+ * continued inputs equals prefill(L1 + L2).  Returns GDN_OK or a negative status.
+ */
+int gdn_prefill_chunked(float *S, const void *q, const void *k, const void *v,
+                        const float *g, const float *beta, int32_t L, int32_t chunk,
+                        gdn_in_dtype in_dt, const gdn_shape *shp, float *o, void *ws,
+                        size_t ws_bytes, void *hip_stream);
+
+/* Static description of a gdn_status value; never NULL. */
+const char *gdn_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */
