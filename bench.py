@@ -1,0 +1,301 @@
+#!/usr/bin/env python3
+"""Benchmark of the GDN speculative-verify hot path on one MI355X.
+
+A step is one speculative pass over a 48-GDN-layer model (32 heads per layer,
+dk = dv = 128, bf16 q/k/v, fp32 state): gdn_verify_block on a T = 8 block for
+all 48 layers in one launch, then gdn_commit at the pass's accepted length
+n ~ Uniform{0..8} (the same n for all layers of a pass), read on the device.
+The headline value is committed tokens per second.
+
+The chunked prefill (one layer, 32 heads, 4,096-token prompt, chunk 64) is
+timed in the same run and reported beside it.
+
+Inputs are synthetic (speculative_verify_amd.inputs) and already resident in
+HBM.  Four independent buffer sets rotate across passes and each commit lags
+its verify by two passes, so no kernel finds its state still in the 256 MB
+Infinity Cache from the previous kernel; every step still does exactly one
+48-layer verify and one 48-layer commit.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+KERNEL_SOURCES = ["speculative_verify_amd/csrc/verify.hip", "speculative_verify_amd/csrc/commit.hip",
+                  "speculative_verify_amd/csrc/prefill.hip", "speculative_verify_amd/csrc/gdn_internal.h"]
+
+# Workload sizes.
+LAYERS, HEADS, DK, DV, T = 48, 32, 128, 128, 8
+PF_B, PF_H, PF_L, PF_C = 1, 32, 4096, 64
+RING, LAG = 4, 2
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=500)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--prefill-reps", type=int, default=20)
+    p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-budget-s", type=float, default=15.0)
+    return p.parse_args()
+
+
+def verify_bytes(B, H, dk, dv, T, es):
+    """Algorithmic HBM bytes of one verify launch: state read once, the block's
+    inputs read once, outputs and the block record written once."""
+    state = B * H * dv * dk * 4
+    inputs = B * T * H * (2 * dk + dv) * es + B * T * H * 8
+    outputs = B * T * H * dv * 4
+    record = B * T * H * (dv * 4 + dk * es + 4) + B * 16
+    return state + inputs + outputs + record
+
+
+def commit_bytes(B, H, dk, dv, n, es):
+    """Algorithmic HBM bytes of one commit launch at accepted length n (same n
+    for every instance): the state read and written once when n >= 1, plus the
+    record rows it replays; n = 0 touches only the control words."""
+    ctrl = B * (16 + 4 + 4)
+    if n == 0:
+        return ctrl
+    return 2 * B * H * dv * dk * 4 + B * n * H * (dv * 4 + dk * es + 4) + ctrl
+
+
+def prefill_bytes(B, H, dk, dv, L):
+    return B * L * H * (2 * dk + dv) * 2 + B * L * H * 8 + B * L * H * dv * 4 + 2 * B * H * dv * dk * 4
+
+
+def prefill_flops(B, H, dk, dv, L, C):
+    """Causal flop count of the chunk form per token and head:
+    state-coupled 6 dk dv (K S^T, Q S^T, the state update), intra-chunk
+    C (3 dk + 2 dv) (causal halves of K K^T, Q K^T, Tm V, Tm K and P D) and the
+    triangular solve C^2 / 3."""
+    per = 6 * dk * dv + C * (3 * dk + 2 * dv) + C * C / 3
+    return B * L * H * per
+
+
+def sources_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, only if
+    it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("sources_sha256_16") != sources_hash():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(args):
+    """The fp64 oracle on a bounded sample of the same pass: verify + commit of
+    the 48-layer block, repeated until about cpu_budget_s seconds of work."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from speculative_verify_amd.inputs import make_accepts, make_inputs
+
+    x = make_inputs(LAYERS, HEADS, DK, DV, T, seed=args.seed + 1000)
+    f64 = [t.double().numpy() for t in (x.S0, x.q, x.k, x.v, x.g, x.beta)]
+    ns = make_accepts(64, T, seed=args.seed + 1000).numpy()
+    passes, tokens = 0, 0
+    t0 = time.perf_counter()
+    while True:
+        n = int(ns[passes % len(ns)])
+        oracle.verify(*f64)
+        oracle.commit(*f64, np.full(LAYERS, n, np.int32))
+        passes += 1
+        tokens += n
+        if time.perf_counter() - t0 >= args.cpu_budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{passes} passes (48 layers x 32 heads, d=128, T=8, verify + commit at "
+                      f"n~U{{0..8}}, {tokens} tokens) in {dt:.1f} s, fp64"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the GDN path is "
+              f"single-GPU by design and has no multi-GPU mode.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import speculative_verify_amd.gdn as G
+    from speculative_verify_amd.inputs import make_accepts, make_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    dt = torch.bfloat16
+    es = 2
+
+    # Buffer sets: state, block inputs, outputs, record.
+    sets = []
+    for r in range(RING):
+        x = make_inputs(LAYERS, HEADS, DK, DV, T, dtype=dt, seed=args.seed + r, device=dev,
+                        device_gen=True)
+        o = torch.empty(LAYERS, T, HEADS, DV, dtype=torch.float32, device=dev)
+        rec = G.new_record(x.S0, T, dt)
+        sets.append((x, o, rec))
+    total = args.warmup + args.steps
+    n_host = make_accepts(total, T, seed=args.seed)
+    n_dev = n_host.view(total, 1).expand(total, LAYERS).contiguous().to(dev)
+    pos = torch.zeros(LAYERS, dtype=torch.int32, device=dev)
+
+    # Pass p is verified on buffer set p % RING and committed LAG steps later:
+    # step s verifies pass s + LAG and commits pass s with n_host[s].
+    def verify(p):
+        x, o, rec = sets[p % RING]
+        G.gdn_verify_block(x.S0, x.q, x.k, x.v, x.g, x.beta, o, rec)
+
+    def commit(p):
+        x, _, rec = sets[p % RING]
+        G.gdn_commit(x.S0, rec, n_dev[p], pos)
+
+    for p in range(LAG):
+        verify(p)
+
+    def step(s, evs=None):
+        if evs is not None:
+            evs[0].record()
+        verify(s + LAG)
+        if evs is not None:
+            evs[1].record()
+        commit(s)
+        if evs is not None:
+            evs[2].record()
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+
+    # Timed region: exactly `steps` passes, events on the launch stream.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    n_timed = [int(v) for v in n_host[args.warmup:total]]
+    tokens = sum(n_timed)
+    t_ver = [evs[i][0].elapsed_time(evs[i][1]) for i in range(args.steps)]
+    t_com = [evs[i][1].elapsed_time(evs[i][2]) for i in range(args.steps)]
+    avg_ver_ms = sum(t_ver) / len(t_ver)
+    avg_com_ms = sum(t_com) / len(t_com)
+    vb = verify_bytes(LAYERS, HEADS, DK, DV, T, es)
+    cb_avg = sum(commit_bytes(LAYERS, HEADS, DK, DV, n, es) for n in n_timed) / len(n_timed)
+    ver_gbs = vb / (avg_ver_ms * 1e-3) / 1e9
+    com_gbs = cb_avg / (avg_com_ms * 1e-3) / 1e9
+    pass_gbs = (vb + cb_avg) / ((avg_ver_ms + avg_com_ms) * 1e-3) / 1e9
+
+    kernels = {
+        "gdn_verify": {"bound": "hbm", "achieved": round(ver_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                       "frac": round(ver_gbs / HBM_PEAK_GBS, 4), "avg_launch_us": round(avg_ver_ms * 1e3, 2),
+                       "algorithmic_bytes_per_launch": vb, "traffic": load_traffic("verify_kernel")},
+        "gdn_commit": {"bound": "hbm", "achieved": round(com_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                       "frac": round(com_gbs / HBM_PEAK_GBS, 4), "avg_launch_us": round(avg_com_ms * 1e3, 2),
+                       "algorithmic_bytes_per_launch": round(cb_avg), "traffic": load_traffic("commit_kernel")},
+    }
+    dominant = "gdn_commit" if avg_com_ms >= avg_ver_ms else "gdn_verify"
+    roof = dict(kernels[dominant])
+    roof["kernel"] = dominant
+
+    result = {
+        "metric": "GDN verify tokens/s (48 layers, T=8) + % HBM peak; prefill tok/s + % MFMA peak",
+        "value": round(tokens / wall, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "speculative verify pass: 48 GDN layers x 32 heads, dk=dv=128, T=8 "
+                               "(7 draft + 1 anchor), bf16 q/k/v, fp32 state, verify + commit at "
+                               "n~U{0..8}",
+                   "layers": LAYERS, "heads": HEADS, "dk": DK, "dv": DV, "T": T,
+                   "input_dtype": "bf16", "tokens_committed": tokens},
+        "rows_per_s": round(T * args.steps / wall, 1),
+        "pass_hbm_frac": round(pass_gbs / HBM_PEAK_GBS, 4),
+        "roofline": roof,
+        "kernels": kernels,
+    }
+
+    if not args.no_prefill:
+        result["prefill"] = bench_prefill(args, G, dev)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args)
+    print(json.dumps(result), flush=True)
+
+
+def bench_prefill(args, G, dev):
+    import torch
+
+    from speculative_verify_amd.inputs import make_inputs
+
+    x = make_inputs(PF_B, PF_H, DK, DV, PF_L, seed=args.seed + 77, device=dev, device_gen=True)
+    o = torch.empty(PF_B, PF_L, PF_H, DV, dtype=torch.float32, device=dev)
+    S = x.S0.clone()
+    try:
+        G.gdn_prefill_chunked(S, x.q, x.k, x.v, x.g, x.beta, o)
+    except G.GdnError as e:
+        return {"status": f"unavailable: {e}"}
+    # A 512 MiB buffer rewritten between reps pushes the prompt out of the caches.
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    t_ms = []
+    for _ in range(args.prefill_reps):
+        flush.fill_(1)
+        S.copy_(x.S0)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        G.gdn_prefill_chunked(S, x.q, x.k, x.v, x.g, x.beta, o)
+        b.record()
+        torch.cuda.synchronize()
+        t_ms.append(a.elapsed_time(b))
+    avg = sum(t_ms) / len(t_ms)
+    fl = prefill_flops(PF_B, PF_H, DK, DV, PF_L, PF_C)
+    by = prefill_bytes(PF_B, PF_H, DK, DV, PF_L)
+    tf = fl / (avg * 1e-3) / 1e12
+    gbs = by / (avg * 1e-3) / 1e9
+    return {"workload": f"chunked prefill: {PF_B} layer x {PF_H} heads, dk=dv={DK}, L={PF_L}, chunk {PF_C}, "
+                        f"bf16 in, fp32 state, cold caches",
+            "tokens_per_s": round(PF_L / (avg * 1e-3), 1), "avg_launch_us": round(avg * 1e3, 2),
+            "mfma": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                     "flops_per_launch": fl, "flop_convention": "causal"},
+            "hbm": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_launch": by,
+                    "traffic": load_traffic("prefill_kernel")}}
+
+
+if __name__ == "__main__":
+    main()

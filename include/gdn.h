@@ -59,7 +59,7 @@ typedef enum gdn_in_dtype {
 
 typedef enum gdn_status {
     GDN_OK = 0,
-    GDN_EINVAL = -1,  /* null or misaligned pointer, unknown dtype */
+    GDN_EINVAL = -1,  /* null or misaligned pointer, unknown or unsupported dtype */
     GDN_EDIM = -2,    /* B or H < 1, dk or dv not in {64, 128}, sizes overflow */
     GDN_ERANGE = -3,  /* T not in [1, 16], L < 0, chunk not 64 */
     GDN_EWS = -4,     /* record or workspace smaller than required */
@@ -157,7 +157,8 @@ size_t gdn_prefill_workspace_bytes(const gdn_shape *shp, int32_t L, int32_t chun
 
 /*
  * Chunked prefill: run the recurrence over an L-token prompt, writing every
- * output and advancing S from the initial to the final state.
+ * output and advancing S from the initial to the final state.  q, k and v must be
+ * bf16 (in_dt == GDN_IN_BF16; GDN_EINVAL otherwise).
  *
  * Source: the devdoido audit, "What does long-context prefill cost on Apple
  * silicon?" (prefill dominates long-context use), with the chunkwise UT/WY form of

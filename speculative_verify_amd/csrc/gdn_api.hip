@@ -1,0 +1,115 @@
+// gdn_api.hip -- the C ABI of libgdn (declared in include/gdn.h): host-side
+// argument checks, record and workspace sizing, and kernel dispatch.  Every check
+// here runs before anything is launched, so a bad argument never reaches the GPU.
+#include <limits.h>
+
+#include <vector>
+
+#include "gdn_internal.h"
+
+using namespace gdn;
+
+namespace {
+
+bool aligned(const void *p, size_t a) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_shape(const gdn_shape *s) {
+    if (!s) return GDN_EINVAL;
+    if (s->B < 1 || s->H < 1) return GDN_EDIM;
+    if ((s->dk != 64 && s->dk != 128) || (s->dv != 64 && s->dv != 128)) return GDN_EDIM;
+    if (int64_t(s->B) * s->H > INT_MAX / 4) return GDN_EDIM;  // grid size and 32-bit row counters
+    return GDN_OK;
+}
+
+bool valid_dtype(int dt) { return dt == GDN_IN_F32 || dt == GDN_IN_BF16; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+size_t gdn_block_record_bytes(const gdn_shape *shp, int32_t T, gdn_in_dtype in_dt) {
+    if (check_shape(shp) != GDN_OK || T < 1 || T > GDN_T_MAX || !valid_dtype(in_dt)) return 0;
+    return rec_layout(shp->B, T, shp->H, shp->dk, shp->dv, esize_of(in_dt)).total;
+}
+
+int gdn_verify_block(const float *S, const void *q, const void *k, const void *v, const float *g,
+                     const float *beta, int32_t T, gdn_in_dtype in_dt, const gdn_shape *shp,
+                     float *o, void *record, size_t record_bytes, void *hip_stream) {
+    int rc = check_shape(shp);
+    if (rc != GDN_OK) return rc;
+    if (!valid_dtype(in_dt)) return GDN_EINVAL;
+    if (!aligned(S, 16) || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) ||
+        !aligned(o, 16) || !aligned(record, 16) || !aligned(g, 4) || !aligned(beta, 4))
+        return GDN_EINVAL;
+    if (T < 1 || T > GDN_T_MAX) return GDN_ERANGE;
+    if (record_bytes < gdn_block_record_bytes(shp, T, in_dt)) return GDN_EWS;
+    return hip_status(launch_verify(S, q, k, v, g, beta, T, in_dt, *shp, o, record,
+                                    static_cast<hipStream_t>(hip_stream)));
+}
+
+int gdn_commit(float *S, void *record, const int32_t *n_accepted, int32_t *pos,
+               const gdn_shape *shp, void *hip_stream) {
+    int rc = check_shape(shp);
+    if (rc != GDN_OK) return rc;
+    if (!aligned(S, 16) || !aligned(record, 16) || !aligned(n_accepted, 4)) return GDN_EINVAL;
+    if (pos != nullptr && !aligned(pos, 4)) return GDN_EINVAL;
+    return hip_status(launch_commit(S, record, n_accepted, pos, *shp,
+                                    static_cast<hipStream_t>(hip_stream)));
+}
+
+int gdn_record_status(const void *record, const gdn_shape *shp, int32_t *host_err_bits,
+                      void *hip_stream) {
+    int rc = check_shape(shp);
+    if (rc != GDN_OK) return rc;
+    if (!aligned(record, 16) || host_err_bits == nullptr) return GDN_EINVAL;
+    std::vector<RecCtrl> ctrl(size_t(shp->B));
+    hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    hipError_t e = hipMemcpyAsync(ctrl.data(), static_cast<const uint8_t *>(record) + 256,
+                                  ctrl.size() * sizeof(RecCtrl), hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return GDN_EHIP;
+    for (int b = 0; b < shp->B; ++b) host_err_bits[b] = int32_t(ctrl[size_t(b)].err);
+    return GDN_OK;
+}
+
+size_t gdn_prefill_workspace_bytes(const gdn_shape *shp, int32_t L, int32_t chunk) {
+    (void)shp;
+    (void)L;
+    (void)chunk;
+    return 0;
+}
+
+int gdn_prefill_chunked(float *S, const void *q, const void *k, const void *v, const float *g,
+                        const float *beta, int32_t L, int32_t chunk, gdn_in_dtype in_dt,
+                        const gdn_shape *shp, float *o, void *ws, size_t ws_bytes,
+                        void *hip_stream) {
+    (void)ws;
+    int rc = check_shape(shp);
+    if (rc != GDN_OK) return rc;
+    if (in_dt != GDN_IN_BF16) return GDN_EINVAL;  // the chunk kernel takes bf16 q, k, v
+    if (L < 0 || chunk != GDN_PREFILL_CHUNK) return GDN_ERANGE;
+    if (ws_bytes < gdn_prefill_workspace_bytes(shp, L, chunk)) return GDN_EWS;
+    if (L == 0) return GDN_OK;
+    if (!aligned(S, 16) || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) ||
+        !aligned(o, 16) || !aligned(g, 4) || !aligned(beta, 4))
+        return GDN_EINVAL;
+    if (int64_t(L) * shp->B * shp->H > int64_t(INT_MAX)) return GDN_EDIM;
+    return hip_status(launch_prefill(S, q, k, v, g, beta, L, in_dt, *shp, o,
+                                     static_cast<hipStream_t>(hip_stream)));
+}
+
+const char *gdn_strerror(int status) {
+    switch (status) {
+        case GDN_OK: return "ok";
+        case GDN_EINVAL: return "invalid argument: null or misaligned pointer, or unknown dtype";
+        case GDN_EDIM: return "invalid shape: B, H >= 1 and dk, dv in {64, 128} required";
+        case GDN_ERANGE: return "out of range: T in [1, 16], L >= 0 and chunk == 64 required";
+        case GDN_EWS: return "record or workspace buffer too small";
+        case GDN_EHIP: return "HIP runtime error";
+        default: return "unknown gdn status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,116 @@
+// gdn_internal.h -- shared internals of libgdn: block-record layout, small device
+// helpers and the launcher declarations.  Not part of the public ABI (include/gdn.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_bf16.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "gdn.h"
+
+namespace gdn {
+
+// ---------------------------------------------------------------------------
+// Block record.  gdn_verify_block writes it, gdn_commit consumes it.
+//
+//   [0, 256)            RecHeader (one per record)
+//   ctrl                RecCtrl[B]                  per-instance control words
+//   G                   fp32 [B][T][H]              log-decay prefix sums of the block
+//   delta               fp32 [B][T][H][dv]          the block's delta rows
+//   kcopy               in_dt [B][T][H][dk]         the block's keys
+//
+// Each section starts on a 256-byte boundary.  Since the verify never writes S,
+// S itself is the block checkpoint; with delta and k the commit rebuilds
+//   S_n = exp(G_n) S + sum_{j<=n} exp(G_n - G_j) delta_j k_j^T.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kRecMagic = 0x52444E47u;   // "GDNR": header written by a verify
+constexpr uint32_t kRecValid = 0x444C4156u;   // "VALD": a block is pending for that instance
+
+struct RecHeader {
+    uint32_t magic;
+    int32_t T, B, H, dk, dv, in_dt;
+    uint32_t reserved[9];
+};
+static_assert(sizeof(RecHeader) == 64, "record header is 64 bytes");
+
+struct RecCtrl {
+    uint32_t valid;  // kRecValid while a verified block is pending
+    uint32_t err;    // GDN_REC_* bits left by the last commit attempt
+    uint32_t done;   // commit workgroups of this instance that finished
+    uint32_t pad;
+};
+static_assert(sizeof(RecCtrl) == 16, "record control word is 16 bytes");
+
+struct RecLayout {
+    size_t ctrl, G, delta, kcopy, total;
+};
+
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+__host__ __device__ inline RecLayout rec_layout(int B, int T, int H, int dk, int dv, int esize) {
+    RecLayout r;
+    r.ctrl = 256;
+    r.G = r.ctrl + align256(size_t(B) * sizeof(RecCtrl));
+    r.delta = r.G + align256(size_t(B) * T * H * sizeof(float));
+    r.kcopy = r.delta + align256(size_t(B) * T * H * dv * sizeof(float));
+    r.total = r.kcopy + align256(size_t(B) * T * H * dk * esize);
+    return r;
+}
+
+inline int esize_of(gdn_in_dtype dt) { return dt == GDN_IN_BF16 ? 2 : 4; }
+
+// ---------------------------------------------------------------------------
+// Device helpers.
+// ---------------------------------------------------------------------------
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ inline float bf16_bits_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+// Load 8 consecutive input elements (16 B of bf16 or 32 B of fp32) as fp32.
+template <typename TIn> struct In8;
+template <> struct In8<float> {
+    float4 a, b;
+    __device__ inline void load(const float *p) {
+        a = *reinterpret_cast<const float4 *>(p);
+        b = *reinterpret_cast<const float4 *>(p + 4);
+    }
+    __device__ inline void store_raw(float *p) const {
+        *reinterpret_cast<float4 *>(p) = a;
+        *reinterpret_cast<float4 *>(p + 4) = b;
+    }
+    __device__ inline float get(int e) const {
+        return e < 4 ? (&a.x)[e] : (&b.x)[e - 4];
+    }
+};
+template <> struct In8<__hip_bfloat16> {
+    uint4 raw;
+    __device__ inline void load(const __hip_bfloat16 *p) { raw = *reinterpret_cast<const uint4 *>(p); }
+    __device__ inline void store_raw(__hip_bfloat16 *p) const { *reinterpret_cast<uint4 *>(p) = raw; }
+    __device__ inline float get(int e) const {
+        const uint32_t w = (&raw.x)[e >> 1];
+        return bf16_bits_to_f32(uint16_t((e & 1) ? (w >> 16) : (w & 0xffffu)));
+    }
+};
+
+template <typename TIn> __device__ inline float load1(const TIn *p);
+template <> __device__ inline float load1<float>(const float *p) { return *p; }
+template <> __device__ inline float load1<__hip_bfloat16>(const __hip_bfloat16 *p) {
+    return bf16_bits_to_f32(*reinterpret_cast<const uint16_t *>(p));
+}
+
+// ---------------------------------------------------------------------------
+// Launchers (one per kernel family); each returns a hipError_t.
+// ---------------------------------------------------------------------------
+hipError_t launch_verify(const float *S, const void *q, const void *k, const void *v,
+                         const float *g, const float *beta, int T, gdn_in_dtype dt,
+                         const gdn_shape &shp, float *o, void *record, hipStream_t stream);
+
+hipError_t launch_commit(float *S, void *record, const int32_t *n_accepted, int32_t *pos,
+                         const gdn_shape &shp, hipStream_t stream);
+
+hipError_t launch_prefill(float *S, const void *q, const void *k, const void *v,
+                          const float *g, const float *beta, int L, gdn_in_dtype dt,
+                          const gdn_shape &shp, float *o, hipStream_t stream);
+
+}  // namespace gdn

@@ -1,0 +1,192 @@
+"""Python binding of libgdn (include/gdn.h), by ctypes.
+
+Argument marshalling only: every function checks that the torch tensors it is
+handed match the layouts the C ABI documents, passes raw device pointers and
+the current HIP stream, and raises GdnError on a non-zero status.  All
+arithmetic happens in libgdn's HIP kernels.  There is no fallback: if
+libgdn.so is missing the import fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgdn.so")
+
+GDN_IN_F32 = 0
+GDN_IN_BF16 = 1
+GDN_T_MAX = 16
+GDN_PREFILL_CHUNK = 64
+GDN_REC_NO_BLOCK = 1
+GDN_REC_N_RANGE = 2
+GDN_REC_SHAPE = 4
+
+EXPORTED = (
+    "gdn_block_record_bytes",
+    "gdn_verify_block",
+    "gdn_commit",
+    "gdn_record_status",
+    "gdn_prefill_workspace_bytes",
+    "gdn_prefill_chunked",
+    "gdn_strerror",
+)
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status} ({strerror(status)})")
+        self.status = status
+
+
+class gdn_shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("dk", ctypes.c_int32),
+                ("dv", ctypes.c_int32)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m speculative_verify_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
+    sp = ctypes.POINTER(gdn_shape)
+    lib.gdn_block_record_bytes.restype = sz
+    lib.gdn_block_record_bytes.argtypes = [sp, i32, ctypes.c_int]
+    lib.gdn_verify_block.restype = ctypes.c_int
+    lib.gdn_verify_block.argtypes = [vp] * 6 + [i32, ctypes.c_int, sp, vp, vp, sz, vp]
+    lib.gdn_commit.restype = ctypes.c_int
+    lib.gdn_commit.argtypes = [vp, vp, vp, vp, sp, vp]
+    lib.gdn_record_status.restype = ctypes.c_int
+    lib.gdn_record_status.argtypes = [vp, sp, ctypes.POINTER(i32), vp]
+    lib.gdn_prefill_workspace_bytes.restype = sz
+    lib.gdn_prefill_workspace_bytes.argtypes = [sp, i32, i32]
+    lib.gdn_prefill_chunked.restype = ctypes.c_int
+    lib.gdn_prefill_chunked.argtypes = [vp] * 6 + [i32, i32, ctypes.c_int, sp, vp, vp, sz, vp]
+    lib.gdn_strerror.restype = ctypes.c_char_p
+    lib.gdn_strerror.argtypes = [ctypes.c_int]
+    return lib
+
+
+lib = _load()
+
+
+def strerror(status: int) -> str:
+    return lib.gdn_strerror(int(status)).decode()
+
+
+def _dt(x: torch.Tensor) -> int:
+    if x.dtype == torch.bfloat16:
+        return GDN_IN_BF16
+    if x.dtype == torch.float32:
+        return GDN_IN_F32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {x.dtype}")
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, torch.Tensor):
+        if not x.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+        return ctypes.c_void_p(x.data_ptr())
+    return ctypes.c_void_p(int(x))
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _shape_of(S: torch.Tensor) -> gdn_shape:
+    if S.dtype != torch.float32 or S.dim() != 4:
+        raise ValueError("S must be fp32 [B][H][dv][dk]")
+    B, H, dv, dk = S.shape
+    return gdn_shape(B, H, dk, dv)
+
+
+def _check_rows(shp: gdn_shape, q, k, v, g, beta, o):
+    B, H, dk, dv = shp.B, shp.H, shp.dk, shp.dv
+    T = q.shape[1]
+    want = {"q": (q, (B, T, H, dk)), "k": (k, (B, T, H, dk)), "v": (v, (B, T, H, dv)),
+            "g": (g, (B, T, H)), "beta": (beta, (B, T, H)), "o": (o, (B, T, H, dv))}
+    for name, (x, shape) in want.items():
+        if tuple(x.shape) != shape:
+            raise ValueError(f"{name} has shape {tuple(x.shape)}, expected {shape}")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must share one dtype")
+    for name, x in (("g", g), ("beta", beta), ("o", o)):
+        if x.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+    return T
+
+
+def gdn_block_record_bytes(B: int, H: int, dk: int, dv: int, T: int, dtype) -> int:
+    dt = _dt(torch.empty(0, dtype=dtype))
+    return int(lib.gdn_block_record_bytes(ctypes.byref(gdn_shape(B, H, dk, dv)), T, dt))
+
+
+def new_record(S: torch.Tensor, T: int, dtype) -> torch.Tensor:
+    """A zero-filled device buffer sized for blocks of T rows of S's shape."""
+    B, H, dv, dk = S.shape
+    n = gdn_block_record_bytes(B, H, dk, dv, T, dtype)
+    if n == 0:
+        raise ValueError("invalid shape, T or dtype for a block record")
+    return torch.zeros(n, dtype=torch.uint8, device=S.device)
+
+
+def gdn_verify_block(S, q, k, v, g, beta, o, record, stream=None) -> None:
+    """o[:] = outputs of the T-row block (q, k, v, g, beta) from checkpoint S; the
+    record becomes the pending block.  S is not modified."""
+    shp = _shape_of(S)
+    T = _check_rows(shp, q, k, v, g, beta, o)
+    rc = lib.gdn_verify_block(_ptr(S), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), T,
+                              _dt(q), ctypes.byref(shp), _ptr(o), _ptr(record),
+                              record.numel() * record.element_size(), _stream(stream))
+    if rc != 0:
+        raise GdnError(rc, "gdn_verify_block")
+
+
+def gdn_commit(S, record, n_accepted, pos=None, stream=None) -> None:
+    """S <- state after the first n_accepted[b] rows of the pending block
+    (device int32 [B]); pos[b] += n_accepted[b] when pos is given."""
+    shp = _shape_of(S)
+    for name, x in (("n_accepted", n_accepted), ("pos", pos)):
+        if x is not None and (x.dtype != torch.int32 or tuple(x.shape) != (shp.B,)):
+            raise ValueError(f"{name} must be int32 [{shp.B}]")
+    rc = lib.gdn_commit(_ptr(S), _ptr(record), _ptr(n_accepted), _ptr(pos), ctypes.byref(shp),
+                        _stream(stream))
+    if rc != 0:
+        raise GdnError(rc, "gdn_commit")
+
+
+def gdn_record_status(record, S, stream=None) -> list[int]:
+    """Per-instance GDN_REC_* error bits of the last commit (synchronising)."""
+    shp = _shape_of(S)
+    out = (ctypes.c_int32 * shp.B)()
+    rc = lib.gdn_record_status(_ptr(record), ctypes.byref(shp), out, _stream(stream))
+    if rc != 0:
+        raise GdnError(rc, "gdn_record_status")
+    return list(out)
+
+
+def gdn_prefill_workspace_bytes(S, L: int, chunk: int = GDN_PREFILL_CHUNK) -> int:
+    return int(lib.gdn_prefill_workspace_bytes(ctypes.byref(_shape_of(S)), L, chunk))
+
+
+def gdn_prefill_chunked(S, q, k, v, g, beta, o, chunk: int = GDN_PREFILL_CHUNK, ws=None,
+                        stream=None) -> None:
+    """Run the prompt (q, k, v, g, beta) through the recurrence: o[:] = all outputs,
+    S advanced in place to the final state."""
+    shp = _shape_of(S)
+    L = _check_rows(shp, q, k, v, g, beta, o)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    rc = lib.gdn_prefill_chunked(_ptr(S), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), L,
+                                 chunk, _dt(q), ctypes.byref(shp), _ptr(o), _ptr(ws), ws_bytes,
+                                 _stream(stream))
+    if rc != 0:
+        raise GdnError(rc, "gdn_prefill_chunked")

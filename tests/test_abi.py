@@ -1,0 +1,99 @@
+"""C-ABI checks that need no GPU: libgdn.so loads, exports every function that
+include/gdn.h declares, and rejects bad host-side arguments with the documented
+status before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+@pytest.fixture(scope="module")
+def G():
+    so = os.path.join(ROOT, "speculative_verify_amd", "libgdn.so")
+    if not os.path.exists(so):
+        from speculative_verify_amd import build
+        build.build()
+    import speculative_verify_amd.gdn as G
+    return G
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(G):
+    names = declared_functions()
+    assert len(names) >= 7
+    assert sorted(G.EXPORTED) == names
+    lib = ctypes.CDLL(G.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(G):
+    for s in (0, -1, -2, -3, -4, -5, 17):
+        assert len(G.strerror(s)) > 0
+
+
+def _shape(B=1, H=2, dk=64, dv=64):
+    import speculative_verify_amd.gdn as G
+    return ctypes.byref(G.gdn_shape(B, H, dk, dv))
+
+
+FAKE = ctypes.c_void_p(1 << 20)        # 16-byte aligned, never dereferenced
+FAKE_ODD = ctypes.c_void_p((1 << 20) + 4)
+
+
+def verify_call(G, S=FAKE, T=8, dt=0, shp=None, rec_bytes=1 << 30, q=FAKE, g=FAKE):
+    return G.lib.gdn_verify_block(S, q, FAKE, FAKE, g, FAKE, T, dt, shp or _shape(), FAKE, FAKE,
+                                  rec_bytes, None)
+
+
+def test_verify_rejects_bad_arguments(G):
+    assert verify_call(G, S=None) == -1
+    assert verify_call(G, q=FAKE_ODD) == -1
+    assert verify_call(G, dt=7) == -1
+    assert verify_call(G, shp=_shape(dk=96)) == -2
+    assert verify_call(G, shp=_shape(B=0)) == -2
+    assert verify_call(G, shp=_shape(dv=32)) == -2
+    assert verify_call(G, T=0) == -3
+    assert verify_call(G, T=17) == -3
+    need = G.lib.gdn_block_record_bytes(_shape(), 8, 0)
+    assert verify_call(G, rec_bytes=need - 1) == -4
+    assert G.lib.gdn_verify_block(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 0, None, FAKE, FAKE,
+                                  1 << 30, None) == -1
+
+
+def test_commit_and_prefill_reject_bad_arguments(G):
+    assert G.lib.gdn_commit(None, FAKE, FAKE, None, _shape(), None) == -1
+    assert G.lib.gdn_commit(FAKE, FAKE, None, None, _shape(), None) == -1
+    assert G.lib.gdn_commit(FAKE, FAKE, FAKE, None, _shape(H=0), None) == -2
+    pf = lambda L=64, chunk=64, dt=1, S=FAKE, shp=None: G.lib.gdn_prefill_chunked(
+        S, FAKE, FAKE, FAKE, FAKE, FAKE, L, chunk, dt, shp or _shape(), FAKE, None, 0, None)
+    assert pf(chunk=32) == -3
+    assert pf(L=-1) == -3
+    assert pf(dt=3) == -1
+    assert pf(S=None) == -1
+    assert pf(shp=_shape(dk=32)) == -2
+    assert pf(L=0, S=None) == 0          # an empty prompt is a no-op
+    assert G.lib.gdn_record_status(FAKE, _shape(), None, None) == -1
+
+
+def test_record_size_accounts_for_payload(G):
+    for (B, H, dk, dv, T, dt) in [(1, 2, 64, 64, 8, torch.float32), (48, 32, 128, 128, 8, torch.bfloat16),
+                                  (3, 5, 128, 64, 16, torch.bfloat16), (2, 1, 64, 128, 1, torch.float32)]:
+        n = G.gdn_block_record_bytes(B, H, dk, dv, T, dt)
+        es = 2 if dt == torch.bfloat16 else 4
+        payload = B * T * H * (4 + 4 * dv + es * dk) + 16 * B
+        assert payload < n <= payload + 5 * 256 + 256
+        assert n % 256 == 0
+    assert G.lib.gdn_block_record_bytes(_shape(), 0, 0) == 0
+    assert G.lib.gdn_block_record_bytes(_shape(), 8, 5) == 0
+    assert G.lib.gdn_prefill_workspace_bytes(_shape(), 4096, 64) == 0
