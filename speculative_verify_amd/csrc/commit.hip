@@ -11,14 +11,16 @@
 //
 // n = 0 touches nothing, so a full rollback is bit-exact.  Each workgroup owns
 // 32 value rows of one head; it reads them and writes them once (n + 1 FMA per
-// element, far below the VALU ridge, so the kernel streams at HBM speed).
+// element, far below the VALU ridge, so the kernel streams at HBM speed).  Each
+// workgroup checks and clears its own pending-block flag, so workgroups never
+// wait on or count each other.
 #include "gdn_internal.h"
 
 namespace gdn {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kRows = 32;
+constexpr int kRows = kCommitRows;
 
 template <int DK, int DV>
 __global__ __launch_bounds__(kThreads) void commit_kernel(float *__restrict__ S,
@@ -30,8 +32,10 @@ __global__ __launch_bounds__(kThreads) void commit_kernel(float *__restrict__ S,
     constexpr int F4_ROW = DK / 4;                       // float4 per state row
     constexpr int NP = kRows * F4_ROW / kThreads;        // float4 per thread
     static_assert(NP >= 1 && kRows * F4_ROW == NP * kThreads, "tiling");
+    static_assert(SLICES <= kCommitSlices, "one pending flag per commit workgroup");
+    static_assert(GDN_T_MAX * kRows % kThreads == 0 && GDN_T_MAX * (DK / 8) <= kThreads, "staging");
 
-    __shared__ float cd[GDN_T_MAX][kRows];                            // exp(G_n-G_j) delta_j
+    __shared__ __attribute__((aligned(16))) float cd[GDN_T_MAX][kRows];  // exp(G_n-G_j) delta_j
     __shared__ __attribute__((aligned(16))) float kk[GDN_T_MAX][DK];  // k_j
 
     const int wg = blockIdx.x;
@@ -54,83 +58,107 @@ __global__ __launch_bounds__(kThreads) void commit_kernel(float *__restrict__ S,
         if (leader && b < hd->B) atomicOr(&ctrl[b].err, uint32_t(GDN_REC_SHAPE));
         return;
     }
-    RecCtrl &c = ctrl[b];
+    const RecLayout RL = rec_layout(B, T, H, DK, DV, in_dt == GDN_IN_BF16 ? 2 : 4);
+    uint32_t *flag = reinterpret_cast<uint32_t *>(rec + RL.flags) + size_t(bh) * kCommitSlices + slice;
     const int n = n_acc[b];
-    if (c.valid != kRecValid) {
-        if (leader) atomicOr(&c.err, uint32_t(GDN_REC_NO_BLOCK));
+    // Every workgroup of an instance sees the same header and n, and its own flag,
+    // which the same verify set for all of them: they all take the same branch.
+    if (*flag != kRecValid) {
+        if (leader) atomicOr(&ctrl[b].err, uint32_t(GDN_REC_NO_BLOCK));
         return;
     }
     if (n < 0 || n > T) {
-        if (leader) atomicOr(&c.err, uint32_t(GDN_REC_N_RANGE));
+        if (leader) atomicOr(&ctrl[b].err, uint32_t(GDN_REC_N_RANGE));
         return;
     }
 
     if (n > 0) {
-        const RecLayout RL = rec_layout(B, T, H, DK, DV, in_dt == GDN_IN_BF16 ? 2 : 4);
+        // Thread tid owns rows 4 (tid / F4_ROW) + p, p < NP, at columns 4 (tid % F4_ROW)..+3:
+        // one 16-byte LDS read of k_j and one of the rows' coefficients per term.
         float4 *Sh = reinterpret_cast<float4 *>(S + size_t(bh) * DV * DK + size_t(slice) * kRows * DK);
+        const int c4 = tid % F4_ROW, r0 = NP * (tid / F4_ROW);
         float4 s[NP];
 #pragma unroll
-        for (int p = 0; p < NP; ++p) s[p] = Sh[tid + kThreads * p];
+        for (int p = 0; p < NP; ++p) s[p] = Sh[(r0 + p) * F4_ROW + c4];
 
         const float *G = reinterpret_cast<const float *>(rec + RL.G);
         const float *D = reinterpret_cast<const float *>(rec + RL.delta);
         const float Gn = G[(size_t(b) * T + (n - 1)) * H + h];
-        for (int idx = tid; idx < n * kRows; idx += kThreads) {
-            const int j = idx / kRows, r = idx - j * kRows;
-            const size_t row = size_t(b) * T + j;
-            cd[j][r] = expf(Gn - G[row * H + h]) * D[(row * H + h) * DV + slice * kRows + r];
+        // Stage the n replayed rows.  Loads read clamped, always-valid rows and
+        // are masked at the store, so they issue back to back.
+        constexpr int CDP = GDN_T_MAX * kRows / kThreads;  // cd entries per thread
+#pragma unroll
+        for (int u = 0; u < CDP; ++u) {
+            const int idx = tid + u * kThreads, j = idx / kRows, r = idx - j * kRows;
+            const size_t row = size_t(b) * T + min(j, n - 1);
+            const float val = expf(Gn - G[row * H + h]) * D[(row * H + h) * DV + slice * kRows + r];
+            if (j < n) cd[j][r] = val;
         }
-        if (in_dt == GDN_IN_BF16) {
-            const uint16_t *K = reinterpret_cast<const uint16_t *>(rec + RL.kcopy);
-            for (int idx = tid; idx < n * DK; idx += kThreads) {
-                const int j = idx / DK, m = idx - j * DK;
-                kk[j][m] = bf16_bits_to_f32(K[((size_t(b) * T + j) * H + h) * DK + m]);
+        {
+            constexpr int PIECES = DK / 8;  // 8-element pieces per key row
+            const int j = tid / PIECES, col = (tid - j * PIECES) * 8;
+            const size_t off = ((size_t(b) * T + min(j, n - 1)) * H + h) * DK + col;
+            float x[8];
+            if (in_dt == GDN_IN_BF16) {
+                const uint4 raw = *reinterpret_cast<const uint4 *>(
+                    reinterpret_cast<const uint16_t *>(rec + RL.kcopy) + off);
+                const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    x[2 * e] = __uint_as_float(w4[e] << 16);
+                    x[2 * e + 1] = __uint_as_float(w4[e] & 0xffff0000u);
+                }
+            } else {
+                const float *K = reinterpret_cast<const float *>(rec + RL.kcopy) + off;
+                const float4 a = *reinterpret_cast<const float4 *>(K);
+                const float4 c = *reinterpret_cast<const float4 *>(K + 4);
+                x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+                x[4] = c.x; x[5] = c.y; x[6] = c.z; x[7] = c.w;
             }
-        } else {
-            const float *K = reinterpret_cast<const float *>(rec + RL.kcopy);
-            for (int idx = tid; idx < n * DK; idx += kThreads) {
-                const int j = idx / DK, m = idx - j * DK;
-                kk[j][m] = K[((size_t(b) * T + j) * H + h) * DK + m];
+            if (j < n) {
+                *reinterpret_cast<float4 *>(&kk[j][col]) = make_float4(x[0], x[1], x[2], x[3]);
+                *reinterpret_cast<float4 *>(&kk[j][col + 4]) = make_float4(x[4], x[5], x[6], x[7]);
             }
         }
         __syncthreads();
 
         const float gam = expf(Gn);
+        float4 a[NP];
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
-            const int f = tid + kThreads * p;
-            const int row = f / F4_ROW, c4 = f - row * F4_ROW;
-            float4 a;
-            a.x = gam * s[p].x;
-            a.y = gam * s[p].y;
-            a.z = gam * s[p].z;
-            a.w = gam * s[p].w;
-            for (int j = 0; j < n; ++j) {
-                const float cdj = cd[j][row];
-                const float4 kv = *reinterpret_cast<const float4 *>(&kk[j][4 * c4]);
-                a.x += cdj * kv.x;
-                a.y += cdj * kv.y;
-                a.z += cdj * kv.z;
-                a.w += cdj * kv.w;
-            }
-            Sh[f] = a;
+            a[p].x = gam * s[p].x;
+            a[p].y = gam * s[p].y;
+            a[p].z = gam * s[p].z;
+            a[p].w = gam * s[p].w;
         }
+        for (int j = 0; j < n; ++j) {
+            const float4 kv = *reinterpret_cast<const float4 *>(&kk[j][4 * c4]);
+            float cdj[NP];
+            if constexpr (NP == 4) {
+                const float4 c = *reinterpret_cast<const float4 *>(&cd[j][r0]);
+                cdj[0] = c.x; cdj[1] = c.y; cdj[2] = c.z; cdj[3] = c.w;
+            } else {
+#pragma unroll
+                for (int p = 0; p < NP; ++p) cdj[p] = cd[j][r0 + p];
+            }
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                a[p].x += cdj[p] * kv.x;
+                a[p].y += cdj[p] * kv.y;
+                a[p].z += cdj[p] * kv.z;
+                a[p].w += cdj[p] * kv.w;
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < NP; ++p) Sh[(r0 + p) * F4_ROW + c4] = a[p];
     }
 
-    // The last workgroup of this instance retires the block and advances pos.
-    // Every wave of every workgroup read c.valid above (its value decided a
-    // branch, so the read has completed) before the barrier and the count below,
-    // so no reader can see the block retired early.  The S stores need no
-    // ordering against the count: nothing in this kernel reads them.
+    // Retire this workgroup's share of the block (every wave has read the flag
+    // above, before this barrier) and let one workgroup advance pos.
     __syncthreads();
     if (tid == 0) {
-        const uint32_t old =
-            __hip_atomic_fetch_add(&c.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (old == uint32_t(H) * SLICES - 1u) {
-            c.done = 0u;
-            c.valid = 0u;
-            if (pos) pos[b] += n;
-        }
+        *flag = 0u;
+        if (pos && h == 0 && slice == 0) pos[b] += n;
     }
 }
 

@@ -15,7 +15,9 @@ namespace gdn {
 // Block record.  gdn_verify_block writes it, gdn_commit consumes it.
 //
 //   [0, 256)            RecHeader (one per record)
-//   ctrl                RecCtrl[B]                  per-instance control words
+//   ctrl                RecCtrl[B]                  per-instance error bits
+//   flags               uint32 [B][H][kCommitSlices] pending-block flags, one per
+//                                                   commit workgroup
 //   G                   fp32 [B][T][H]              log-decay prefix sums of the block
 //   delta               fp32 [B][T][H][dv]          the block's delta rows
 //   kcopy               in_dt [B][T][H][dk]         the block's keys
@@ -23,9 +25,13 @@ namespace gdn {
 // Each section starts on a 256-byte boundary.  Since the verify never writes S,
 // S itself is the block checkpoint; with delta and k the commit rebuilds
 //   S_n = exp(G_n) S + sum_{j<=n} exp(G_n - G_j) delta_j k_j^T.
+// Every commit workgroup owns one flag, which the verify sets and the commit
+// checks and clears, so the commit needs no coordination between workgroups.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kRecMagic = 0x52444E47u;   // "GDNR": header written by a verify
-constexpr uint32_t kRecValid = 0x444C4156u;   // "VALD": a block is pending for that instance
+constexpr uint32_t kRecValid = 0x444C4156u;   // "VALD": a block is pending for that workgroup
+constexpr int kCommitRows = 32;               // value rows per commit workgroup
+constexpr int kCommitSlices = 4;              // flags per (instance, head): 128 / kCommitRows
 
 struct RecHeader {
     uint32_t magic;
@@ -35,15 +41,13 @@ struct RecHeader {
 static_assert(sizeof(RecHeader) == 64, "record header is 64 bytes");
 
 struct RecCtrl {
-    uint32_t valid;  // kRecValid while a verified block is pending
     uint32_t err;    // GDN_REC_* bits left by the last commit attempt
-    uint32_t done;   // commit workgroups of this instance that finished
-    uint32_t pad;
+    uint32_t pad[3];
 };
 static_assert(sizeof(RecCtrl) == 16, "record control word is 16 bytes");
 
 struct RecLayout {
-    size_t ctrl, G, delta, kcopy, total;
+    size_t ctrl, flags, G, delta, kcopy, total;
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -51,7 +55,8 @@ __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_
 __host__ __device__ inline RecLayout rec_layout(int B, int T, int H, int dk, int dv, int esize) {
     RecLayout r;
     r.ctrl = 256;
-    r.G = r.ctrl + align256(size_t(B) * sizeof(RecCtrl));
+    r.flags = r.ctrl + align256(size_t(B) * sizeof(RecCtrl));
+    r.G = r.flags + align256(size_t(B) * H * kCommitSlices * sizeof(uint32_t));
     r.delta = r.G + align256(size_t(B) * T * H * sizeof(float));
     r.kcopy = r.delta + align256(size_t(B) * T * H * dv * sizeof(float));
     r.total = r.kcopy + align256(size_t(B) * T * H * dk * esize);

@@ -89,7 +89,9 @@ __global__ __launch_bounds__(64 * NWS) void prefill_kernel(
     constexpr int KT = DK / 16;        // 16-key tiles
     constexpr int KB = DK / 32;        // 32-key contraction blocks
     constexpr int NT = 64 * NWS;
+    constexpr int NLD = C * DK / 8 / NT;  // 16-byte staging pieces per thread per tensor
     static_assert(SLICES * RS == DV && KB >= 1, "tiling");
+    static_assert(NLD >= 1 && NLD * NT * 8 == C * DK, "staging tiling");
 
     __shared__ Smem<DK> sm;
 
@@ -125,48 +127,53 @@ __global__ __launch_bounds__(64 * NWS) void prefill_kernel(
         const int n = min(C, L - c0);
         const size_t row0 = size_t(b) * L + c0;  // (b, c0) token row
 
-        // ---- stage the chunk's keys and queries (rows >= n are zero) ----
-        for (int idx = tid; idx < C * DK / 8; idx += NT) {
-            const int t = idx / (DK / 8), col = (idx - t * (DK / 8)) * 8;
-            uint4 kv = {0u, 0u, 0u, 0u}, qv = {0u, 0u, 0u, 0u};
-            if (t < n) {
-                const size_t off = ((row0 + t) * H + h) * DK + col;
-                kv = *reinterpret_cast<const uint4 *>(k + off);
-                qv = *reinterpret_cast<const uint4 *>(q + off);
-            }
-            *reinterpret_cast<uint4 *>(&sm.Ks[t][col]) = kv;
-            *reinterpret_cast<uint4 *>(&sm.Qs[t][col]) = qv;
-            const __bf16 *kh = reinterpret_cast<const __bf16 *>(&kv);
+        // ---- stage the chunk's keys, queries and gates (rows >= n are zero) ----
+        // Every load is issued before any store, so one memory latency covers them.
+        {
+            uint4 kv[NLD], qv[NLD];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) sm.Kt[col + e][t] = kh[e];
-        }
-        // This lane's values v[t][irow] for t = 16 tt + 4 lg + r.
-        float vv[4][4];
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * tt + 4 * lg + r;
-                vv[tt][r] = t < n ? load1(v + ((row0 + t) * H + h) * DV + irow) : 0.f;
+            for (int u = 0; u < NLD; ++u) {
+                const int idx = tid + u * NT;
+                const int t = idx / (DK / 8), col = (idx - t * (DK / 8)) * 8;
+                // Clamped rows keep every load valid and branch-free; rows past
+                // the prompt are zeroed after the load.
+                const size_t off = ((row0 + min(t, n - 1)) * H + h) * DK + col;
+                kv[u] = *reinterpret_cast<const uint4 *>(k + off);
+                qv[u] = *reinterpret_cast<const uint4 *>(q + off);
+                if (t >= n) {
+                    kv[u] = make_uint4(0u, 0u, 0u, 0u);
+                    qv[u] = make_uint4(0u, 0u, 0u, 0u);
+                }
             }
-        if (w == 0) {
-            float gt = 0.f, bt = 0.f;
-            if (lane < n) {
-                const size_t gi = (row0 + lane) * H + h;
-                gt = g[gi];
-                bt = beta[gi];
+            const size_t gi = (row0 + min(lane, n - 1)) * H + h;
+            float gt = g[gi], bt = beta[gi];
+            if (lane >= n) {
+                gt = 0.f;
+                bt = 0.f;
             }
-            float Gp = gt;  // inclusive prefix sum over the chunk
 #pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float y = __shfl_up(Gp, off, 64);
-                if (lane >= off) Gp += y;
+            for (int u = 0; u < NLD; ++u) {
+                const int idx = tid + u * NT;
+                const int t = idx / (DK / 8), col = (idx - t * (DK / 8)) * 8;
+                *reinterpret_cast<uint4 *>(&sm.Ks[t][col]) = kv[u];
+                *reinterpret_cast<uint4 *>(&sm.Qs[t][col]) = qv[u];
+                const __bf16 *kh = reinterpret_cast<const __bf16 *>(&kv[u]);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) sm.Kt[col + e][t] = kh[e];
             }
-            const float Glast = __shfl(Gp, n - 1, 64);
-            sm.G[lane] = Gp;
-            sm.gam[lane] = __expf(Gp);
-            sm.ee[lane] = lane < n ? __expf(Glast - Gp) : 0.f;
-            sm.bet[lane] = bt;
+            if (w == 0) {
+                float Gp = gt;  // inclusive prefix sum over the chunk
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const float y = __shfl_up(Gp, off, 64);
+                    if (lane >= off) Gp += y;
+                }
+                const float Glast = __shfl(Gp, n - 1, 64);
+                sm.G[lane] = Gp;
+                sm.gam[lane] = __expf(Gp);
+                sm.ee[lane] = lane < n ? __expf(Glast - Gp) : 0.f;
+                sm.bet[lane] = bt;
+            }
         }
         __syncthreads();
 
@@ -208,6 +215,7 @@ __global__ __launch_bounds__(64 * NWS) void prefill_kernel(
 #pragma unroll
                 for (int jj = 0; jj < r; ++jj) acc -= sm.Am[base + r][base + jj] * x[jj];
                 x[r] = acc;
+                asm volatile("" ::: "memory");  // keep each row's loads with its row (register pressure)
             }
 #pragma unroll
             for (int r = 0; r < 16; ++r) sm.Tm[base + r][base + lr] = x[r];
@@ -243,6 +251,15 @@ __global__ __launch_bounds__(64 * NWS) void prefill_kernel(
         // The contraction over keys visits, for block p and lane group lg, keys
         // 32p + 4lg + {0..3} and 32p + 16 + 4lg + {0..3}: the keys this lane holds
         // in st[2p] and st[2p+1].
+        float vv[4][4];  // v[t][irow] for t = 16 tt + 4 lg + r
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * tt + 4 * lg + r;
+                const float x = load1(v + ((row0 + min(t, n - 1)) * H + h) * DV + irow);
+                vv[tt][r] = t < n ? x : 0.f;
+            }
         Split8 sB[KB];
 #pragma unroll
         for (int p = 0; p < KB; ++p) {
@@ -250,33 +267,25 @@ __global__ __launch_bounds__(64 * NWS) void prefill_kernel(
                                 st[2 * p + 1][0], st[2 * p + 1][1], st[2 * p + 1][2], st[2 * p + 1][3]};
             sB[p] = split8(x);
         }
-        f32x4 X[4], Y[4];
+        // R = diag(beta) (V - diag(gamma) K S^T), rows t = 16 tt + 4 lg + r.
+        float R[4][4];
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
-            X[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            Y[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            f32x4 X = {0.f, 0.f, 0.f, 0.f};
             const int t = 16 * tt + lr;
 #pragma unroll
             for (int p = 0; p < KB; ++p) {
                 const bf16x8 ka = cat4(*reinterpret_cast<const bf16x4 *>(&sm.Ks[t][32 * p + 4 * lg]),
                                        *reinterpret_cast<const bf16x4 *>(&sm.Ks[t][32 * p + 16 + 4 * lg]));
-                const bf16x8 qa = cat4(*reinterpret_cast<const bf16x4 *>(&sm.Qs[t][32 * p + 4 * lg]),
-                                       *reinterpret_cast<const bf16x4 *>(&sm.Qs[t][32 * p + 16 + 4 * lg]));
-                X[tt] = mma(ka, sB[p].hi, X[tt]);
-                X[tt] = mma(ka, sB[p].lo, X[tt]);
-                Y[tt] = mma(qa, sB[p].hi, Y[tt]);
-                Y[tt] = mma(qa, sB[p].lo, Y[tt]);
+                X = mma(ka, sB[p].hi, X);
+                X = mma(ka, sB[p].lo, X);
             }
-        }
-        // R = diag(beta) (V - diag(gamma) K S^T), rows t = 16 tt + 4 lg + r.
-        float R[4][4];
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int t = 16 * tt + 4 * lg + r;
-                R[tt][r] = sm.bet[t] * (vv[tt][r] - sm.gam[t] * X[tt][r]);
+                const int tr = 16 * tt + 4 * lg + r;
+                R[tt][r] = sm.bet[tr] * (vv[tt][r] - sm.gam[tr] * X[r]);
             }
+        }
         // D = Linv R (Linv is lower triangular: only blocks p <= tt / 2).
         Split8 rB[2];
 #pragma unroll
@@ -308,22 +317,31 @@ __global__ __launch_bounds__(64 * NWS) void prefill_kernel(
         }
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
-            f32x4 O2 = {0.f, 0.f, 0.f, 0.f};
+            f32x4 Y = {0.f, 0.f, 0.f, 0.f};
             const int t = 16 * tt + lr;
+#pragma unroll
+            for (int p = 0; p < KB; ++p) {
+                const bf16x8 qa = cat4(*reinterpret_cast<const bf16x4 *>(&sm.Qs[t][32 * p + 4 * lg]),
+                                       *reinterpret_cast<const bf16x4 *>(&sm.Qs[t][32 * p + 16 + 4 * lg]));
+                Y = mma(qa, sB[p].hi, Y);
+                Y = mma(qa, sB[p].lo, Y);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Y[r] *= sm.gam[16 * tt + 4 * lg + r];
 #pragma unroll
             for (int p = 0; p <= tt / 2; ++p) {
                 const float4 a0 = *reinterpret_cast<const float4 *>(&sm.Pm[t][32 * p + 4 * lg]);
                 const float4 a1 = *reinterpret_cast<const float4 *>(&sm.Pm[t][32 * p + 16 + 4 * lg]);
                 const float x[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-                O2 = mma3(split8(x), dB[p], O2);
+                Y = mma3(split8(x), dB[p], Y);
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int tr = 16 * tt + 4 * lg + r;
-                if (tr < n) o[((row0 + tr) * H + h) * DV + irow] = sm.gam[tr] * Y[tt][r] + O2[r];
+                if (tr < n) o[((row0 + tr) * H + h) * DV + irow] = Y[r];
             }
         }
-        // S <- gamma_last S + K^T diag(e) D, result tiles over keys match st[][].
+        // S <- gamma_last S + K^T diag(e) D; the result tiles over keys match st[][].
         Split8 eB[2];
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
@@ -370,29 +388,18 @@ hipError_t launch_t(float *S, const void *q, const void *k, const void *v, const
     return hipGetLastError();
 }
 
-// Value rows per workgroup: the widest slice that still gives every CU a
-// workgroup; narrower slices trade redundant per-chunk work for parallelism.
-template <int DK, int DV>
-hipError_t launch_dk_dv(float *S, const void *q, const void *k, const void *v, const float *g,
-                        const float *beta, int L, const gdn_shape &s, float *o, hipStream_t st) {
-    const long heads = long(s.B) * s.H;
-    if (DV >= 128 && heads * (DV / 128) >= 256)
-        return launch_t<DK, DV, (DV >= 128 ? 8 : 2)>(S, q, k, v, g, beta, L, s, o, st);
-    if (heads * (DV / 64) >= 256)
-        return launch_t<DK, DV, 4>(S, q, k, v, g, beta, L, s, o, st);
-    return launch_t<DK, DV, 2>(S, q, k, v, g, beta, L, s, o, st);
-}
-
 }  // namespace
 
+// One workgroup per (instance, head): the chunk's shared quantities (Gram
+// matrices, Linv, gates) are built once per head, and each wave owns 16 value rows.
 hipError_t launch_prefill(float *S, const void *q, const void *k, const void *v, const float *g,
                           const float *beta, int L, gdn_in_dtype dt, const gdn_shape &shp, float *o,
                           hipStream_t stream) {
     if (dt != GDN_IN_BF16) return hipErrorInvalidValue;
-    if (shp.dk == 128 && shp.dv == 128) return launch_dk_dv<128, 128>(S, q, k, v, g, beta, L, shp, o, stream);
-    if (shp.dk == 128 && shp.dv == 64) return launch_dk_dv<128, 64>(S, q, k, v, g, beta, L, shp, o, stream);
-    if (shp.dk == 64 && shp.dv == 128) return launch_dk_dv<64, 128>(S, q, k, v, g, beta, L, shp, o, stream);
-    return launch_dk_dv<64, 64>(S, q, k, v, g, beta, L, shp, o, stream);
+    if (shp.dk == 128 && shp.dv == 128) return launch_t<128, 128, 8>(S, q, k, v, g, beta, L, shp, o, stream);
+    if (shp.dk == 128 && shp.dv == 64) return launch_t<128, 64, 4>(S, q, k, v, g, beta, L, shp, o, stream);
+    if (shp.dk == 64 && shp.dv == 128) return launch_t<64, 128, 8>(S, q, k, v, g, beta, L, shp, o, stream);
+    return launch_t<64, 64, 4>(S, q, k, v, g, beta, L, shp, o, stream);
 }
 
 }  // namespace gdn

@@ -91,8 +91,8 @@ def test_record_size_accounts_for_payload(G):
                                   (3, 5, 128, 64, 16, torch.bfloat16), (2, 1, 64, 128, 1, torch.float32)]:
         n = G.gdn_block_record_bytes(B, H, dk, dv, T, dt)
         es = 2 if dt == torch.bfloat16 else 4
-        payload = B * T * H * (4 + 4 * dv + es * dk) + 16 * B
-        assert payload < n <= payload + 5 * 256 + 256
+        payload = B * T * H * (4 + 4 * dv + es * dk) + 16 * B + 16 * B * H
+        assert payload < n <= payload + 6 * 256 + 256
         assert n % 256 == 0
     assert G.lib.gdn_block_record_bytes(_shape(), 0, 0) == 0
     assert G.lib.gdn_block_record_bytes(_shape(), 8, 5) == 0
