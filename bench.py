@@ -49,6 +49,9 @@ def parse():
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget-s", type=float, default=15.0)
+    p.add_argument("--copy-calibration-mib", type=int, default=0,
+                   help="after the bench, run 3 plain device copies of this many MiB (a "
+                        "reference kernel of known traffic for hardware counters)")
     return p.parse_args()
 
 
@@ -254,6 +257,14 @@ def main():
         result["prefill"] = bench_prefill(args, G, dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args)
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 18  # fp32 elements
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_calibration"] = {"bytes_read": n * 4, "bytes_written": n * 4, "launches": 3}
     print(json.dumps(result), flush=True)
 
 

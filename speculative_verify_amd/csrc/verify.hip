@@ -1,12 +1,14 @@
 // verify.hip -- the verify kernel: outputs of a T-row speculative block from the
 // checkpoint state, without writing the state.
 //
-// One single-wave workgroup owns 16 value rows of one (instance, head): its
-// slice of the dv x dk fp32 state is read from HBM exactly once, into registers,
-// and never written (the value-column partition of the lithos-metal README, "How
-// it works", region table, "GDN mixer" row).  Rows of S never interact, so the
-// slices need no communication; single-wave workgroups need no barriers, and
-// thousands of them keep loads of some waves overlapped with MFMA work of others.
+// A workgroup owns one (instance, head); each of its waves owns 64 value rows,
+// whose dv x dk fp32 state is read from HBM exactly once, into registers, and
+// never written (the value-column partition of the lithos-metal README, "How it
+// works", region table, "GDN mixer" row).  At 128 state registers per lane and
+// three waves per SIMD, the 96 MiB state of a 48-layer, 32-head batch is resident
+// in the register files at once: every load is issued up front, in one round.  The
+// block coefficients depend only on q and k, which arrive first, so they are
+// ready before the state is.
 //
 // Instead of stepping the state T times in registers (about 3T FMA per state
 // element), the block is solved in its UT form with chunk = T.  With
@@ -30,207 +32,279 @@ __device__ inline float comp(const float4 &v, int c) {
 }
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
-// Four consecutive input elements: the A operand of one fp32 MFMA k-step group.
-template <typename TIn> struct X4;
-template <> struct X4<float> {
-    float4 v;
-    __device__ inline void load(const float *p) { v = *reinterpret_cast<const float4 *>(p); }
-    __device__ inline void zero() { v = make_float4(0.f, 0.f, 0.f, 0.f); }
-    __device__ inline void store(float *p) const { *reinterpret_cast<float4 *>(p) = v; }
-    __device__ inline float f(int c) const { return comp(v, c); }
-};
-template <> struct X4<__hip_bfloat16> {
-    uint2 v;
-    __device__ inline void load(const __hip_bfloat16 *p) { v = *reinterpret_cast<const uint2 *>(p); }
-    __device__ inline void zero() { v = make_uint2(0u, 0u); }
-    __device__ inline void store(__hip_bfloat16 *p) const { *reinterpret_cast<uint2 *>(p) = v; }
-    __device__ inline float f(int c) const {
-        const uint32_t w = c < 2 ? v.x : v.y;
-        return __uint_as_float((c & 1) ? (w & 0xffff0000u) : (w << 16));
-    }
-};
-
-__device__ inline bf16x8 cat_bf16(const uint2 &a, const uint2 &b) {
-    const uint4 u = make_uint4(a.x, a.y, b.x, b.y);
-    return __builtin_bit_cast(bf16x8, u);
-}
-
-// Workgroup id -> (head, 16-row slice).  Workgroups are dealt to the 8 XCDs in
-// id order, so within each run of 8 * SL ids the XCD index picks the head and
-// the rest picks the slice: all slices of a head run on one XCD and share its L2
-// for the head's q, k and v rows.
-template <int SL>
-__device__ inline void map_workgroup(int id, int nheads, int &bh, int &sl) {
-    constexpr int G8 = 8 * SL;
-    const int full = nheads / 8;
-    const int grp = id / G8;
-    if (grp < full) {
-        const int rem = id - grp * G8;
-        bh = grp * 8 + (rem & 7);
-        sl = rem >> 3;
-    } else {
-        const int r2 = id - full * G8;
-        bh = full * 8 + r2 / SL;
-        sl = r2 - (r2 / SL) * SL;
+// Split eight fp32 values (two float4) into high and low bf16 parts:
+// x = hi + lo + r with |r| <= 2^-17 |x|; products with exact bf16 operands are
+// exact in the fp32 MFMA accumulator.
+__device__ inline void split_bf16(const float4 &a, const float4 &b, bf16x8 &hi, bf16x8 &lo) {
+    const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const __bf16 hh = static_cast<__bf16>(x[e]);
+        hi[e] = hh;
+        lo[e] = static_cast<__bf16>(x[e] - static_cast<float>(hh));
     }
 }
 
-// One wave owns 16 value rows of one (instance, head).
+// A operand row x of the bf16 X for key block p: keys 16(2p) + 4lg + {0..3} in
+// slots 0..3 and 16(2p+1) + 4lg + {0..3} in slots 4..7 (the keys a lane holds in
+// its state registers for that block).
+__device__ inline bf16x8 xrow_bf16(const __bf16 *Xb, int stride, int x, int p, int lg) {
+    const bf16x4 lo4 = *reinterpret_cast<const bf16x4 *>(Xb + x * stride + 32 * p + 4 * lg);
+    const bf16x4 hi4 = *reinterpret_cast<const bf16x4 *>(Xb + x * stride + 32 * p + 16 + 4 * lg);
+    return __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 // X rows: 0..T-1 hold k_1..k_T, T..2T-1 hold q_1..q_T, the rest are zero.
 // MT = number of 16-row MFMA tiles of X (1 for T <= 8, 2 for T <= 16).
 template <int DK, int DV, typename TIn, int MT>
-__global__ __launch_bounds__(64) void verify_kernel(
+__global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void verify_kernel(
     const float *__restrict__ S, const TIn *__restrict__ q, const TIn *__restrict__ k,
     const TIn *__restrict__ v, const float *__restrict__ g, const float *__restrict__ beta,
     int T, int B, int H, float *__restrict__ o, uint8_t *__restrict__ rec) {
+    constexpr int NW = DV / 64;      // waves per workgroup
+    constexpr int NTH = 64 * NW;     // threads
+    constexpr int NT = 4;            // 16-row MFMA tiles per wave (64 rows)
     constexpr int KM = DK / 16;      // 16-key groups (4 keys per lane group)
     constexpr int XR = 16 * MT;      // rows of X
+    constexpr int XS = DK + 4;       // LDS row stride of X, floats
     constexpr int TM = 8 * MT;       // largest T for this instantiation
-    constexpr int SL = DV / 16;      // 16-row slices per head
+    constexpr int KH = KM / NW;      // key groups per wave for the Gram matrix
+    constexpr int NCH = (2 * TM * DK / 8 + NTH - 1) / NTH;  // 8-element X pieces per thread
+    constexpr int NVP = (TM * DV / 8 + NTH - 1) / NTH;      // 8-element V pieces per thread
     constexpr bool kBf16 = sizeof(TIn) == 2;
+    static_assert(NW * 64 == DV && KH * NW == KM, "shape");
 
-    __shared__ float Pw[XR][17];                     // [K;Q] S^T for this wave's rows
+    // X as fp32 (fp32 inputs) or as the exact bf16 inputs (bf16 inputs).
+    constexpr int XSB = DK + 8;      // LDS row stride of the bf16 X, elements
+    __shared__ __attribute__((aligned(16))) float X[kBf16 ? 4 : XR * XS];
+    __shared__ __attribute__((aligned(16))) __bf16 Xb[kBf16 ? XR * XSB : 8];
+    __shared__ __attribute__((aligned(16))) float Vs[TM][DV];   // the block's values
+    __shared__ float P[XR][DV + 1];               // [K;Q] S^T: rows x, columns value row
+    __shared__ float gpart[NW][XR][XR + 1];       // per-wave partial Gram matrices
     __shared__ float coefM[TM][TM + 1], coefN[TM][TM + 1];
     __shared__ float Gs[TM], gam[TM], bs[TM];
 
-    int bh, sl;
-    map_workgroup<SL>(blockIdx.x, B * H, bh, sl);
+    const int bh = blockIdx.x;
     const int b = bh / H, h = bh - b * H;
-    const int lane = threadIdx.x, lr = lane & 15, lg = lane >> 4;
-    const int row0 = sl * 16;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lr = lane & 15, lg = lane >> 4;
     const RecLayout RL = rec_layout(B, T, H, DK, DV, int(sizeof(TIn)));
 
-    // 1. The slice's state: row row0 + lr, keys 16m + 4lg .. +3.  Issued first so
-    //    all of it is in flight together.
-    const float *Srow = S + (size_t(bh) * DV + row0 + lr) * DK + 4 * lg;
-    float4 sreg[KM];
+    // Loads, in the order they are consumed; every address is valid (clamped) and
+    // no loaded register is touched until it is used, so all of them are in
+    // flight together.
+    // 1. The block's keys, queries and values, 8 elements per piece.
+    In8<TIn> xin[NCH], vin[NVP];
 #pragma unroll
-    for (int m = 0; m < KM; ++m) sreg[m] = *reinterpret_cast<const float4 *>(Srow + 16 * m);
-
-    // 2. X rows for the A operands, straight from global memory (the head's rows
-    //    are shared by its slices through L2).  Every load below reads a valid
-    //    address (indices are clamped) and is masked afterwards: branch-free loads
-    //    issue back to back instead of each waiting for all earlier ones.
-    X4<TIn> xa[MT][KM];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        const int x = 16 * mt + lr;
-        const bool isk = x < T, live = x < 2 * T;
-        const int t = isk ? x : min(x - T, T - 1);
-        const TIn *src = (isk ? k : q) + (size_t(b * T + t) * H + h) * DK;
-#pragma unroll
-        for (int m = 0; m < KM; ++m) {
-            xa[mt][m].load(src + 16 * m + 4 * lg);
-            if (!live) xa[mt][m].zero();
-        }
+    for (int u = 0; u < NCH; ++u) {
+        const int c = min(tid + u * NTH, 2 * T * DK / 8 - 1);
+        const int e = c * 8, r = e / DK, col = e - r * DK;
+        const bool isk = r < T;
+        const int t = isk ? r : r - T;
+        xin[u].load((isk ? k : q) + (size_t(b * T + t) * H + h) * DK + col);
     }
-    // 3. Value column of this lane's row for the row phase (lanes 0..15 use it).
-    float vreg[TM];
 #pragma unroll
-    for (int t = 0; t < TM; ++t)
-        vreg[t] = load1(v + (size_t(b * T + min(t, T - 1)) * H + h) * DV + row0 + lr);
-    // 4. Gates: log-decay prefix sums in one fixed order (the commit reuses them).
-    {
-        float gl[TM];
-#pragma unroll
-        for (int t = 0; t < TM; ++t) {
-            const float gv = g[size_t(b * T + min(t, T - 1)) * H + h];
-            gl[t] = t < T ? gv : 0.f;
-        }
-        const float bl = beta[size_t(b * T + min(lane, T - 1)) * H + h];
-        float pre = 0.f, mine = 0.f;
-#pragma unroll
-        for (int t = 0; t < TM; ++t) {
-            pre += gl[t];
-            if (t == lane) mine = pre;
-        }
-        if (lane < T) {
-            Gs[lane] = mine;
-            gam[lane] = expf(mine);
-            bs[lane] = bl;
-        }
+    for (int u = 0; u < NVP; ++u) {
+        const int c = min(tid + u * NTH, T * DV / 8 - 1);
+        const int e = c * 8, t = e / DV, col = e - t * DV;
+        vin[u].load(v + (size_t(b * T + t) * H + h) * DV + col);
     }
-
-    // 5. [K;Q] S^T on fp32 MFMA; the contraction visits keys 16m + 4lg + c for lane
-    //    group lg, slot c, in A and B alike.
-    f32x4 acc[MT];
+    // 2. Gates: lane t of wave 0 holds g_t and beta_t.
+    const float gv = g[size_t(b * T + min(lane, T - 1)) * H + h];
+    const float bv = beta[size_t(b * T + min(lane, T - 1)) * H + h];
+    // Compiler-only barrier: keep the loads above ahead of the state loads, so
+    // consuming them never waits for the state.
+    asm volatile("" ::: "memory");
+    // 3. The wave's state rows 64w + 16nt + lr, keys 16m + 4lg .. +3, tile by tile.
+    const float *Sw = S + (size_t(bh) * DV + 64 * w + lr) * DK + 4 * lg;
+    float4 sreg[NT][KM];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int m = 0; m < KM; ++m)
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[mt][m].f(c), comp(sreg[m], c),
-                                                               acc[mt], 0, 0, 0);
-    // Gram matrix X X^T.  bf16 rows multiply exactly on bf16 MFMA (keys 16(2p) +
-    // 4lg + {0..3} and 16(2p+1) + 4lg + {0..3} in slots 0..7); fp32 rows use fp32
-    // MFMA.
-    f32x4 gacc[MT][MT];
-#pragma unroll
-    for (int m1 = 0; m1 < MT; ++m1)
-#pragma unroll
-        for (int m2 = 0; m2 < MT; ++m2) gacc[m1][m2] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (kBf16) {
-#pragma unroll
-        for (int p = 0; p < KM / 2; ++p)
-#pragma unroll
-            for (int m1 = 0; m1 < MT; ++m1)
-#pragma unroll
-                for (int m2 = 0; m2 < MT; ++m2)
-                    gacc[m1][m2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        cat_bf16(xa[m1][2 * p].v, xa[m1][2 * p + 1].v),
-                        cat_bf16(xa[m2][2 * p].v, xa[m2][2 * p + 1].v), gacc[m1][m2], 0, 0, 0);
-    } else {
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int m = 0; m < KM; ++m)
+            sreg[nt][m] = *reinterpret_cast<const float4 *>(Sw + size_t(16 * nt) * DK + 16 * m);
+
+    // Stage X and V (fp32) and the keys' record copy; zero the padding rows.  The
+    // piece index is clamped exactly as for the loads: a thread past the end
+    // rewrites the last piece with the same data.  Unconditional use keeps the
+    // compiler from sinking the loads below the state loads.
+    TIn *kcopy = reinterpret_cast<TIn *>(rec + RL.kcopy);
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
+    for (int u = 0; u < NCH; ++u) {
+        const int c = min(tid + u * NTH, 2 * T * DK / 8 - 1);
+        const int e = c * 8, r = e / DK, col = e - r * DK;
+        if constexpr (kBf16) {
+            xin[u].store_raw(reinterpret_cast<TIn *>(Xb + r * XSB + col));
+        } else {
+            *reinterpret_cast<float4 *>(X + r * XS + col) =
+                make_float4(xin[u].get(0), xin[u].get(1), xin[u].get(2), xin[u].get(3));
+            *reinterpret_cast<float4 *>(X + r * XS + col + 4) =
+                make_float4(xin[u].get(4), xin[u].get(5), xin[u].get(6), xin[u].get(7));
+        }
+        if (r < T) xin[u].store_raw(kcopy + (size_t(b * T + r) * H + h) * DK + col);
+    }
+#pragma unroll
+    for (int u = 0; u < NVP; ++u) {
+        const int c = min(tid + u * NTH, T * DV / 8 - 1);
+        const int e = c * 8, t = e / DV, col = e - t * DV;
+        *reinterpret_cast<float4 *>(&Vs[t][col]) =
+            make_float4(vin[u].get(0), vin[u].get(1), vin[u].get(2), vin[u].get(3));
+        *reinterpret_cast<float4 *>(&Vs[t][col + 4]) =
+            make_float4(vin[u].get(4), vin[u].get(5), vin[u].get(6), vin[u].get(7));
+    }
+    for (int idx = tid; idx < (XR - 2 * T) * DK; idx += NTH) {
+        if constexpr (kBf16)
+            Xb[(2 * T + idx / DK) * XSB + idx % DK] = static_cast<__bf16>(0.f);
+        else
+            X[(2 * T + idx / DK) * XS + idx % DK] = 0.f;
+    }
+    if (w == 0) {
+        // Log-decay prefix sums over the block, in one fixed order (a wave scan);
+        // the commit reuses the stored values.
+        float Gp = lane < T ? gv : 0.f;
+#pragma unroll
+        for (int off = 1; off < TM; off <<= 1) {
+            const float y = __shfl_up(Gp, off, 64);
+            if (lane >= off) Gp += y;
+        }
+        if (lane < T) {
+            Gs[lane] = Gp;
+            gam[lane] = expf(Gp);
+            bs[lane] = bv;
+            reinterpret_cast<float *>(rec + RL.G)[size_t(b * T + lane) * H + h] = Gp;
+        }
+    }
+    __syncthreads();
+
+    // Gram matrix X X^T, each wave over its share of the keys, while the state is
+    // still arriving: exact on bf16 MFMA for bf16 rows, fp32 MFMA otherwise.
+    // Contraction slots visit keys 16(2p) + 4lg + {0..3} and 16(2p+1) + 4lg +
+    // {0..3} (bf16), or 16m + 4lg + c (fp32), in A and B alike.
+    {
+        f32x4 gacc[MT][MT];
+#pragma unroll
+        for (int m1 = 0; m1 < MT; ++m1)
+#pragma unroll
+            for (int m2 = 0; m2 < MT; ++m2) gacc[m1][m2] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (kBf16) {
+#pragma unroll
+            for (int pp = 0; pp < KH / 2; ++pp) {
+                const int p = w * (KH / 2) + pp;
+                bf16x8 a[MT];
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) a[mt] = xrow_bf16(Xb, XSB, 16 * mt + lr, p, lg);
 #pragma unroll
                 for (int m1 = 0; m1 < MT; ++m1)
 #pragma unroll
                     for (int m2 = 0; m2 < MT; ++m2)
-                        gacc[m1][m2] = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                            xa[m1][m].f(c), xa[m2][m].f(c), gacc[m1][m2], 0, 0, 0);
-    }
-
-    // 6. Lane (lr, lg) of a 16x16 result tile holds rows 4lg..4lg+3 of column lr.
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Pw[16 * mt + 4 * lg + r][lr] = acc[mt][r];
-    __syncthreads();
-    //    Block coefficients: coefM[t][j] = beta_t Gamma_tj k_t.k_j (j < t),
-    //    coefN[t][j] = Gamma_tj q_t.k_j (j <= t).
-#pragma unroll
-    for (int m1 = 0; m1 < MT; ++m1)
-#pragma unroll
-        for (int m2 = 0; m2 < MT; ++m2)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int x = 16 * m1 + 4 * lg + r, y = 16 * m2 + lr;
-                const float val = gacc[m1][m2][r];
-                if (x < T && y < x) coefM[x][y] = bs[x] * expf(Gs[x] - Gs[y]) * val;
-                if (x >= T && x < 2 * T && y <= x - T)
-                    coefN[x - T][y] = expf(Gs[x - T] - Gs[y]) * val;
+                        gacc[m1][m2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m1], a[m2], gacc[m1][m2], 0, 0, 0);
             }
+        } else {
+#pragma unroll
+            for (int mm = 0; mm < KH; ++mm) {
+                const int m = w * KH + mm;
+                float4 a[MT];
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    a[mt] = *reinterpret_cast<const float4 *>(X + (16 * mt + lr) * XS + 16 * m + 4 * lg);
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+#pragma unroll
+                    for (int m1 = 0; m1 < MT; ++m1)
+#pragma unroll
+                        for (int m2 = 0; m2 < MT; ++m2)
+                            gacc[m1][m2] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                                comp(a[m1], c), comp(a[m2], c), gacc[m1][m2], 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int m1 = 0; m1 < MT; ++m1)
+#pragma unroll
+            for (int m2 = 0; m2 < MT; ++m2)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) gpart[w][16 * m1 + 4 * lg + r][16 * m2 + lr] = gacc[m1][m2][r];
+    }
+    __syncthreads();
+    // Block coefficients (shared by every value row of the head):
+    //   coefM[t][j] = beta_t Gamma_tj k_t.k_j (j < t),  coefN[t][j] = Gamma_tj q_t.k_j (j <= t).
+    for (int idx = tid; idx < TM * TM; idx += NTH) {
+        const int t = idx / TM, j = idx - t * TM;
+        if (t < T && j <= t) {
+            float kk = 0.f, qk = 0.f;
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww) {
+                kk += gpart[ww][t][j];
+                qk += gpart[ww][T + t][j];
+            }
+            const float dec = expf(Gs[t] - Gs[j]);
+            coefM[t][j] = j < t ? bs[t] * dec * kk : 0.f;
+            coefN[t][j] = dec * qk;
+        }
+    }
     __syncthreads();
 
-    // 7. Value rows (lanes 0..15): forward substitution for delta, then outputs.
-    if (lg == 0) {
-        const int i = row0 + lr;
+    // [K;Q] S^T, tile by tile as the state arrives.  bf16 inputs: the fp32 state
+    // is split into bf16 high and low parts against the exact bf16 X (two bf16
+    // MFMAs per 32 keys); fp32 inputs: fp32 MFMA.  The contraction slots visit the
+    // same keys in A and B.
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        f32x4 acc[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (kBf16) {
+#pragma unroll
+            for (int p = 0; p < KM / 2; ++p) {
+                bf16x8 shi, slo;
+                split_bf16(sreg[nt][2 * p], sreg[nt][2 * p + 1], shi, slo);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    const bf16x8 a = xrow_bf16(Xb, XSB, 16 * mt + lr, p, lg);
+                    acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, shi, acc[mt], 0, 0, 0);
+                    acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, slo, acc[mt], 0, 0, 0);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int m = 0; m < KM; ++m) {
+                float4 a[MT];
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    a[mt] = *reinterpret_cast<const float4 *>(X + (16 * mt + lr) * XS + 16 * m + 4 * lg);
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt)
+                        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(comp(a[mt], c), comp(sreg[nt][m], c),
+                                                                       acc[mt], 0, 0, 0);
+            }
+        }
+        // Lane (lr, lg) of a 16x16 result tile holds rows 4lg..4lg+3 of column lr.
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) P[16 * mt + 4 * lg + r][64 * w + 16 * nt + lr] = acc[mt][r];
+    }
+    // P columns 64w..64w+63 are this wave's own; its LDS operations complete in
+    // order, and the compiler-only barrier keeps the compiler from reordering them.
+    asm volatile("" ::: "memory");
+
+    // Value rows (one per thread): forward substitution for delta, then outputs.
+    {
+        const int i = tid;
         float *Drec = reinterpret_cast<float *>(rec + RL.delta);
         float d[TM];
 #pragma unroll
         for (int t = 0; t < TM; ++t) {
             if (t < T) {
-                float dt = bs[t] * (vreg[t] - gam[t] * Pw[t][lr]);
+                float dt = bs[t] * (Vs[t][i] - gam[t] * P[t][i]);
 #pragma unroll
                 for (int j = 0; j < t; ++j) dt -= coefM[t][j] * d[j];
                 d[t] = dt;
-                float ot = gam[t] * Pw[T + t][lr];
+                float ot = gam[t] * P[T + t][i];
 #pragma unroll
                 for (int j = 0; j <= t; ++j) ot += coefN[t][j] * d[j];
                 const size_t idx = (size_t(b * T + t) * H + h) * DV + i;
@@ -240,20 +314,12 @@ __global__ __launch_bounds__(64) void verify_kernel(
         }
     }
 
-    // 8. Record bookkeeping.  Slice 0 stores the head's gates and keys; the first
-    //    slices set the pending-block flags of the commit workgroups.
-    if (sl == 0) {
-        if (lane < T) reinterpret_cast<float *>(rec + RL.G)[size_t(b * T + lane) * H + h] = Gs[lane];
-        if (lr < T) {
-            TIn *kc = reinterpret_cast<TIn *>(rec + RL.kcopy) + (size_t(b * T + lr) * H + h) * DK + 4 * lg;
-#pragma unroll
-            for (int m = 0; m < KM; ++m) xa[0][m].store(kc + 16 * m);
-        }
-    }
-    if (lane == 0 && sl < DV / kCommitRows)
-        reinterpret_cast<uint32_t *>(rec + RL.flags)[size_t(bh) * kCommitSlices + sl] = kRecValid;
-    if (lane == 0 && sl == 0 && h == 0) reinterpret_cast<RecCtrl *>(rec + RL.ctrl)[b].err = 0u;
-    if (lane == 0 && sl == 0 && bh == 0) {
+    // Mark the block pending for every commit workgroup of this head, clear the
+    // instance's error bits; the header describes the record.
+    if (tid < DV / kCommitRows)
+        reinterpret_cast<uint32_t *>(rec + RL.flags)[size_t(bh) * kCommitSlices + tid] = kRecValid;
+    if (tid == 0 && h == 0) reinterpret_cast<RecCtrl *>(rec + RL.ctrl)[b].err = 0u;
+    if (tid == 0 && bh == 0) {
         RecHeader *hd = reinterpret_cast<RecHeader *>(rec);
         hd->T = T;
         hd->B = B;
@@ -269,7 +335,7 @@ template <int DK, int DV, typename TIn>
 hipError_t launch_t(const float *S, const void *q, const void *k, const void *v, const float *g,
                     const float *beta, int T, const gdn_shape &s, float *o, void *rec,
                     hipStream_t st) {
-    const dim3 grid(unsigned(s.B) * unsigned(s.H) * unsigned(DV / 16)), block(64);
+    const dim3 grid(unsigned(s.B) * unsigned(s.H)), block(DV);
     auto *qq = static_cast<const TIn *>(q);
     auto *kk = static_cast<const TIn *>(k);
     auto *vv = static_cast<const TIn *>(v);
