@@ -150,8 +150,11 @@ int gdn_record_status(const void *record, const gdn_shape *shp, int32_t *host_er
                       void *hip_stream);
 
 /*
- * Bytes of workspace gdn_prefill_chunked needs for prompt length L; 0 means the
- * call needs none (ws may then be NULL).
+ * Bytes of workspace with which gdn_prefill_chunked runs its two-pass schedule
+ * for prompt length L: a parallel pass builds every chunk's state-independent
+ * quantities first, so the sequential chunk scan carries only state-coupled work.
+ * It pays off for few (instance, head) pairs (long scans, idle compute units);
+ * 0 means the one-pass schedule is used for this shape and no workspace helps.
  */
 size_t gdn_prefill_workspace_bytes(const gdn_shape *shp, int32_t L, int32_t chunk);
 
@@ -169,8 +172,10 @@ size_t gdn_prefill_workspace_bytes(const gdn_shape *shp, int32_t L, int32_t chun
  *   q, k, v, g, beta, o   as for the verify, with L rows.  L >= 0 (L = 0 is a
  *            no-op); the last chunk may be partial.
  *   chunk    GDN_PREFILL_CHUNK.
- *   ws       workspace of gdn_prefill_workspace_bytes(...) bytes (may be NULL
- *            when that is 0).
+ *   ws       optional device workspace (16-byte aligned).  With at least
+ *            gdn_prefill_workspace_bytes(...) bytes the two-pass schedule runs;
+ *            with NULL or fewer bytes the one-pass schedule runs.  Results agree
+ *            within rounding either way.
  *
  * Splitting a prompt is exact up to rounding: prefill(L1) then prefill(L2) on the
  * continued inputs equals prefill(L1 + L2).  Returns GDN_OK or a negative status.

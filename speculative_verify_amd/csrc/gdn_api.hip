@@ -75,28 +75,25 @@ int gdn_record_status(const void *record, const gdn_shape *shp, int32_t *host_er
 }
 
 size_t gdn_prefill_workspace_bytes(const gdn_shape *shp, int32_t L, int32_t chunk) {
-    (void)shp;
-    (void)L;
-    (void)chunk;
-    return 0;
+    if (check_shape(shp) != GDN_OK || L < 0 || chunk != GDN_PREFILL_CHUNK) return 0;
+    return prefill_workspace_bytes(*shp, L);
 }
 
 int gdn_prefill_chunked(float *S, const void *q, const void *k, const void *v, const float *g,
                         const float *beta, int32_t L, int32_t chunk, gdn_in_dtype in_dt,
                         const gdn_shape *shp, float *o, void *ws, size_t ws_bytes,
                         void *hip_stream) {
-    (void)ws;
     int rc = check_shape(shp);
     if (rc != GDN_OK) return rc;
-    if (in_dt != GDN_IN_BF16) return GDN_EINVAL;  // the chunk kernel takes bf16 q, k, v
+    if (in_dt != GDN_IN_BF16) return GDN_EINVAL;  // the chunk kernels take bf16 q, k, v
     if (L < 0 || chunk != GDN_PREFILL_CHUNK) return GDN_ERANGE;
-    if (ws_bytes < gdn_prefill_workspace_bytes(shp, L, chunk)) return GDN_EWS;
     if (L == 0) return GDN_OK;
     if (!aligned(S, 16) || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) ||
         !aligned(o, 16) || !aligned(g, 4) || !aligned(beta, 4))
         return GDN_EINVAL;
+    if (ws != nullptr && !aligned(ws, 16)) return GDN_EINVAL;
     if (int64_t(L) * shp->B * shp->H > int64_t(INT_MAX)) return GDN_EDIM;
-    return hip_status(launch_prefill(S, q, k, v, g, beta, L, in_dt, *shp, o,
+    return hip_status(launch_prefill(S, q, k, v, g, beta, L, in_dt, *shp, o, ws, ws_bytes,
                                      static_cast<hipStream_t>(hip_stream)));
 }
 

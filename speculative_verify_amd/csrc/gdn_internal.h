@@ -116,6 +116,11 @@ hipError_t launch_commit(float *S, void *record, const int32_t *n_accepted, int3
 
 hipError_t launch_prefill(float *S, const void *q, const void *k, const void *v,
                           const float *g, const float *beta, int L, gdn_in_dtype dt,
-                          const gdn_shape &shp, float *o, hipStream_t stream);
+                          const gdn_shape &shp, float *o, void *ws, size_t ws_bytes,
+                          hipStream_t stream);
+
+// Workspace bytes the two-pass prefill schedule uses for this shape and prompt
+// length (0 when the one-pass schedule is the faster one).
+size_t prefill_workspace_bytes(const gdn_shape &shp, int L);
 
 }  // namespace gdn

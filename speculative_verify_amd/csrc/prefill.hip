@@ -19,14 +19,22 @@
 // |x - hi - lo| <= 2^-17 |x|, and multiplied as hi*hi + hi*lo + lo*hi (the
 // split-bf16 scheme of Henry, Tang & Heinecke, ARITH 2019).
 //
-// One workgroup owns RS = 16 * NWS value rows of one (instance, head) -- rows of S
-// never interact, so slices of the value index are independent -- and walks the
-// chunks in order with its state slice held in registers.  Wave w owns 16 value
-// rows.  Per chunk, all waves first build the shared chunk quantities (staged
-// keys and queries, gates, Gram matrices, Linv) in LDS, then each wave runs the
-// state-coupled products for its rows.  MFMA results feed the next MFMA straight
-// from registers: a 16x16 result tile holds rows 4*(lane/16)+r of column lane%16,
-// which is the layout of a B operand whose contraction index runs over those rows.
+// Rows of S never interact, so slices of the value index are independent; a
+// workgroup owns RS = 16 * NWS value rows of one (instance, head), holds their
+// state in registers and walks the chunks in order, wave w owning 16 rows.  Per
+// chunk, the state-independent quantities (gates, Gram matrices, Linv, P) are
+// built in LDS, then each wave runs the state-coupled products for its rows.
+// MFMA results feed the next MFMA straight from registers: a 16x16 result tile
+// holds rows 4*(lane/16)+r of column lane%16, which is the layout of a B operand
+// whose contraction index runs over those rows.
+//
+// Two schedules:
+//  - one pass (many heads): one workgroup per head builds and consumes each
+//    chunk's quantities itself;
+//  - two passes (few heads, where the chunk scan's latency dominates): a prep
+//    kernel builds Linv, P and the gates of every chunk in parallel into a
+//    workspace, and a scan kernel walks the chunks doing only state-coupled
+//    work, with the next chunk's operands prefetched in registers.
 #include "gdn_internal.h"
 
 namespace gdn {
@@ -77,8 +85,392 @@ struct alignas(16) Smem {
     float Pm[C][C + 4];     // lower-incl(Gamma_tj q_t.k_j)
     float Wb[3][16][20];    // block-inverse scratch
     float gam[C], ee[C], bet[C], G[C];
+    // Linv and P split into bf16 high and low parts: the A operands of the
+    // state-coupled products, ready to use.
+    __bf16 LiH[C][C + 8], LiL[C][C + 8], PH[C][C + 8], PL[C][C + 8];
 };
 
+// LDS of the prep kernel: Linv and its scratch reuse the keys' and queries'
+// space once the Gram matrices are built, so two workgroups fit on a CU.
+template <int DK>
+struct alignas(16) PrepSmem {
+    union {
+        struct {
+            __bf16 Ks[C][DK + 8];
+            __bf16 Qs[C][DK + 8];
+        };
+        struct {
+            float Tm[C][C + 4];
+            float Wb[3][16][20];
+        };
+    };
+    float Am[C][C + 4];
+    float Pm[C][C + 4];
+    float gam[C], ee[C], bet[C], G[C];
+};
+
+// Workspace record of one (instance, head, chunk) in the two-pass schedule.
+// Linv and P as bf16 (hi, lo) pairs: four [C][C] bf16 arrays, then gam, ee, bet.
+constexpr size_t kPrepMatBytes = 4 * C * C * sizeof(__bf16);
+constexpr size_t kPrepBytes = (kPrepMatBytes + 3 * C * sizeof(float) + 255) & ~size_t(255);
+constexpr int kFewHeads = 256;  // fewer (instance, head) pairs than this: two passes
+
+// Keys and queries of one chunk as raw 16-byte pieces: piece u of thread tid is
+// row t = (tid + u NT) / (DK / 8), columns col .. col + 7.
+template <int DK, int NT>
+struct ChunkKQ {
+    static constexpr int NLD = C * DK / 8 / NT;
+    static_assert(NLD >= 1 && NLD * NT * 8 == C * DK, "staging tiling");
+    uint4 kv[NLD], qv[NLD];
+    // Rows past the prompt read the last valid row (always a valid address); they
+    // are zeroed when stored, never here, so nothing waits on these loads early.
+    __device__ inline void load(const __hip_bfloat16 *k, const __hip_bfloat16 *q, size_t row0, int n,
+                                int H, int h, int tid) {
+#pragma unroll
+        for (int u = 0; u < NLD; ++u) {
+            const int idx = tid + u * NT;
+            const int t = idx / (DK / 8), col = (idx - t * (DK / 8)) * 8;
+            const size_t off = ((row0 + min(t, n - 1)) * H + h) * DK + col;
+            kv[u] = *reinterpret_cast<const uint4 *>(k + off);
+            qv[u] = *reinterpret_cast<const uint4 *>(q + off);
+        }
+    }
+    // kTrans: also write the transposed keys (the state update's A operand).
+    template <bool kTrans = true, typename SM>
+    __device__ inline void store(SM &sm, int n, int tid) const {
+#pragma unroll
+        for (int u = 0; u < NLD; ++u) {
+            const int idx = tid + u * NT;
+            const int t = idx / (DK / 8), col = (idx - t * (DK / 8)) * 8;
+            const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+            const uint4 kk = t < n ? kv[u] : z, qq = t < n ? qv[u] : z;
+            *reinterpret_cast<uint4 *>(&sm.Ks[t][col]) = kk;
+            *reinterpret_cast<uint4 *>(&sm.Qs[t][col]) = qq;
+            if constexpr (kTrans) {
+                const __bf16 *kh = reinterpret_cast<const __bf16 *>(&kk);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) sm.Kt[col + e][t] = kh[e];
+            }
+        }
+    }
+};
+
+// Gates of one chunk (wave 0, lane t): log-decay prefix sum G, gamma = exp(G),
+// e = exp(G_last - G), beta; rows past the prompt get g = beta = e = 0.
+template <typename SM>
+__device__ inline void chunk_gates(SM &sm, float gt, float bt, int n, int lane) {
+    if (lane >= n) {
+        gt = 0.f;
+        bt = 0.f;
+    }
+    float Gp = gt;  // inclusive prefix sum over the chunk
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(Gp, off, 64);
+        if (lane >= off) Gp += y;
+    }
+    const float Glast = __shfl(Gp, n - 1, 64);
+    sm.G[lane] = Gp;
+    sm.gam[lane] = __expf(Gp);
+    sm.ee[lane] = lane < n ? __expf(Glast - Gp) : 0.f;
+    sm.bet[lane] = bt;
+}
+
+// Gram matrices and Linv of the staged chunk (all NWS waves; barriers inside).
+// On entry Ks, Qs and the gates are in LDS; on exit Pm and Tm hold P and Linv in
+// their lower block triangles (diagonal blocks included, zero above the
+// diagonal within them); the strictly upper blocks are never written.
+template <int DK, int NWS, typename SM>
+__device__ inline void chunk_prep(SM &sm, int tid, int w, int lane) {
+    constexpr int KB = DK / 32;
+    constexpr int NT = 64 * NWS;
+    const int lr = lane & 15, lg = lane >> 4;
+    // Gram tiles: A from K K^T, P from Q K^T (lower tiles only).
+    for (int qi = w; qi < 20; qi += NWS) {
+        const bool isq = qi >= 10;
+        const int p = isq ? qi - 10 : qi;
+        const int tt = p >= 6 ? 3 : p >= 3 ? 2 : p >= 1 ? 1 : 0;
+        const int jt = p - tt * (tt + 1) / 2;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const bf16x8 a = isq ? *reinterpret_cast<const bf16x8 *>(&sm.Qs[16 * tt + lr][32 * kb + 8 * lg])
+                                 : *reinterpret_cast<const bf16x8 *>(&sm.Ks[16 * tt + lr][32 * kb + 8 * lg]);
+            const bf16x8 bk = *reinterpret_cast<const bf16x8 *>(&sm.Ks[16 * jt + lr][32 * kb + 8 * lg]);
+            acc = mma(a, bk, acc);
+        }
+        const int j = 16 * jt + lr;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = 16 * tt + 4 * lg + r;
+            const float dec = __expf(sm.G[t] - sm.G[j]);
+            if (isq)
+                sm.Pm[t][j] = j <= t ? dec * acc[r] : 0.f;
+            else
+                sm.Am[t][j] = j < t ? sm.bet[t] * dec * acc[r] : 0.f;
+        }
+    }
+    __syncthreads();
+    // Linv = (I + A)^{-1} by 16x16 blocks.  Diagonal blocks by forward
+    // substitution, lane = (block lg, column lr).
+    if (w == 0) {
+        const int base = 16 * lg;
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float acc = r == lr ? 1.f : 0.f;
+#pragma unroll
+            for (int jj = 0; jj < r; ++jj) acc -= sm.Am[base + r][base + jj] * x[jj];
+            x[r] = acc;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sm.Tm[base + r][base + lr] = x[r];
+    }
+    __syncthreads();
+    // Off-diagonal blocks, one block diagonal at a time:
+    //   X_ij = -X_ii sum_{m=j}^{i-1} A_im X_mj   (i = j + d).
+    for (int d = 1; d <= 3; ++d) {
+        const int npairs = 4 - d;
+        for (int idx = tid; idx < npairs * 256; idx += NT) {
+            const int j = idx >> 8, r = (idx >> 4) & 15, cc = idx & 15;
+            const int i = j + d;
+            float acc = 0.f;
+            for (int mb = j; mb < i; ++mb)
+#pragma unroll
+                for (int m = 0; m < 16; ++m)
+                    acc += sm.Am[16 * i + r][16 * mb + m] * sm.Tm[16 * mb + m][16 * j + cc];
+            sm.Wb[j][r][cc] = acc;
+        }
+        __syncthreads();
+        for (int idx = tid; idx < npairs * 256; idx += NT) {
+            const int j = idx >> 8, r = (idx >> 4) & 15, cc = idx & 15;
+            const int i = j + d;
+            float acc = 0.f;
+#pragma unroll
+            for (int m = 0; m < 16; ++m) acc += sm.Tm[16 * i + r][16 * i + m] * sm.Wb[j][m][cc];
+            sm.Tm[16 * i + r][16 * j + cc] = -acc;
+        }
+        __syncthreads();
+    }
+}
+
+// Eight elements (row t, columns j8 .. j8 + 7) of Linv and of P, split into bf16
+// high and low parts; zero in the strictly upper blocks, which chunk_prep leaves
+// unwritten.
+template <typename SM>
+__device__ inline void split_mats8(const SM &sm, int t, int j8, Split8 &ls, Split8 &ps) {
+    float a[8], p8[8];
+    *reinterpret_cast<float4 *>(a) = *reinterpret_cast<const float4 *>(&sm.Tm[t][j8]);
+    *reinterpret_cast<float4 *>(a + 4) = *reinterpret_cast<const float4 *>(&sm.Tm[t][j8 + 4]);
+    *reinterpret_cast<float4 *>(p8) = *reinterpret_cast<const float4 *>(&sm.Pm[t][j8]);
+    *reinterpret_cast<float4 *>(p8 + 4) = *reinterpret_cast<const float4 *>(&sm.Pm[t][j8 + 4]);
+    if ((j8 >> 4) > (t >> 4)) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] = p8[e] = 0.f;
+    }
+    ls = split8(a);
+    ps = split8(p8);
+}
+
+// The state-coupled products' A operands in LDS: Linv and P split.
+template <int DK, int NT>
+__device__ inline void split_mats(Smem<DK> &sm, int tid) {
+    for (int idx = tid; idx < C * C / 8; idx += NT) {
+        const int t = idx / (C / 8), j8 = (idx - t * (C / 8)) * 8;
+        Split8 ls, ps;
+        split_mats8(sm, t, j8, ls, ps);
+        *reinterpret_cast<bf16x8 *>(&sm.LiH[t][j8]) = ls.hi;
+        *reinterpret_cast<bf16x8 *>(&sm.LiL[t][j8]) = ls.lo;
+        *reinterpret_cast<bf16x8 *>(&sm.PH[t][j8]) = ps.hi;
+        *reinterpret_cast<bf16x8 *>(&sm.PL[t][j8]) = ps.lo;
+    }
+    __syncthreads();
+}
+
+// Scheduling fences between the steps of chunk_state (compiler-only; no
+// instruction is emitted).  They keep the scheduler from hoisting the next
+// step's LDS operands, and the registers they hold, over the current step: a
+// gain where the chunk's own prep shares the kernel, a loss in the scan kernel,
+// whose prefetch needs the freedom.
+template <bool F>
+__device__ inline void step_fence() {
+    if constexpr (F) asm volatile("" ::: "memory");
+}
+template <bool F>
+__device__ inline void sched_fence() {
+    if constexpr (F) __builtin_amdgcn_sched_barrier(0);
+}
+
+// State-coupled products of one chunk for one wave's 16 value rows (value row
+// irow = this lane's column).  vv[tt][r] = v[t][irow] for t = 16 tt + 4 lg + r
+// (0 past the prompt); obase points at o for the chunk's first token and this
+// lane's value row, ostride is one token.
+template <int DK, bool F>
+__device__ inline void chunk_state(const Smem<DK> &sm, float (&st)[DK / 16][4], const float (&vv)[4][4],
+                                   int n, int lane, float *__restrict__ obase, size_t ostride) {
+    constexpr int KT = DK / 16, KB = DK / 32;
+    const int lr = lane & 15, lg = lane >> 4;
+    // The contraction over keys visits, for block p and lane group lg, keys
+    // 32p + 4lg + {0..3} and 32p + 16 + 4lg + {0..3}: the keys this lane holds
+    // in st[2p] and st[2p+1].  Products are formed in an order that keeps few
+    // values live: K S^T and Q S^T first (the split state then dies), then D, then
+    // the outputs and the state update.
+    f32x4 X[4], Y[4];
+    {
+        Split8 sB[KB];
+#pragma unroll
+        for (int p = 0; p < KB; ++p) {
+            const float x[8] = {st[2 * p][0], st[2 * p][1], st[2 * p][2], st[2 * p][3],
+                                st[2 * p + 1][0], st[2 * p + 1][1], st[2 * p + 1][2], st[2 * p + 1][3]};
+            sB[p] = split8(x);
+        }
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            X[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            Y[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const int t = 16 * tt + lr;
+#pragma unroll
+            for (int p = 0; p < KB; ++p) {
+                const bf16x8 ka = cat4(*reinterpret_cast<const bf16x4 *>(&sm.Ks[t][32 * p + 4 * lg]),
+                                       *reinterpret_cast<const bf16x4 *>(&sm.Ks[t][32 * p + 16 + 4 * lg]));
+                const bf16x8 qa = cat4(*reinterpret_cast<const bf16x4 *>(&sm.Qs[t][32 * p + 4 * lg]),
+                                       *reinterpret_cast<const bf16x4 *>(&sm.Qs[t][32 * p + 16 + 4 * lg]));
+                X[tt] = mma(ka, sB[p].hi, X[tt]);
+                X[tt] = mma(ka, sB[p].lo, X[tt]);
+                Y[tt] = mma(qa, sB[p].hi, Y[tt]);
+                Y[tt] = mma(qa, sB[p].lo, Y[tt]);
+            }
+            sched_fence<F>();
+        }
+    }
+    step_fence<F>();
+    // R = diag(beta) (V - diag(gamma) K S^T), rows t = 16 tt + 4 lg + r, split as the
+    // B operand of D = Linv R.
+    Split8 rB[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int tt = 2 * p + (e >> 2), r = e & 3, tr = 16 * tt + 4 * lg + r;
+            x[e] = sm.bet[tr] * (vv[tt][r] - sm.gam[tr] * X[tt][r]);
+        }
+        rB[p] = split8(x);
+    }
+    // D = Linv R (Linv is lower triangular: only blocks p <= tt / 2).
+    f32x4 D[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+        D[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int t = 16 * tt + lr;
+#pragma unroll
+        for (int p = 0; p <= tt / 2; ++p) {
+            Split8 a;
+            a.hi = cat4(*reinterpret_cast<const bf16x4 *>(&sm.LiH[t][32 * p + 4 * lg]),
+                        *reinterpret_cast<const bf16x4 *>(&sm.LiH[t][32 * p + 16 + 4 * lg]));
+            a.lo = cat4(*reinterpret_cast<const bf16x4 *>(&sm.LiL[t][32 * p + 4 * lg]),
+                        *reinterpret_cast<const bf16x4 *>(&sm.LiL[t][32 * p + 16 + 4 * lg]));
+            D[tt] = mma3(a, rB[p], D[tt]);
+        }
+        sched_fence<F>();
+    }
+    step_fence<F>();
+    // D split twice: as is (for P D) and scaled by e (for the state update).
+    Split8 dB[2], eB[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        float x[8], y[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int tt = 2 * p + (e >> 2), r = e & 3, tr = 16 * tt + 4 * lg + r;
+            x[e] = D[tt][r];
+            y[e] = sm.ee[tr] * D[tt][r];
+        }
+        dB[p] = split8(x);
+        eB[p] = split8(y);
+    }
+    step_fence<F>();
+    // O = diag(gamma) Q S^T + P D.
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+        const int t = 16 * tt + lr;
+        f32x4 Ot = Y[tt];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Ot[r] *= sm.gam[16 * tt + 4 * lg + r];
+#pragma unroll
+        for (int p = 0; p <= tt / 2; ++p) {
+            Split8 a;
+            a.hi = cat4(*reinterpret_cast<const bf16x4 *>(&sm.PH[t][32 * p + 4 * lg]),
+                        *reinterpret_cast<const bf16x4 *>(&sm.PH[t][32 * p + 16 + 4 * lg]));
+            a.lo = cat4(*reinterpret_cast<const bf16x4 *>(&sm.PL[t][32 * p + 4 * lg]),
+                        *reinterpret_cast<const bf16x4 *>(&sm.PL[t][32 * p + 16 + 4 * lg]));
+            Ot = mma3(a, dB[p], Ot);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int tr = 16 * tt + 4 * lg + r;
+            if (tr < n) obase[size_t(tr) * ostride] = Ot[r];
+        }
+        sched_fence<F>();
+    }
+    step_fence<F>();
+    // S <- gamma_last S + K^T diag(e) D; the result tiles over keys match st[][].
+    const float glast = sm.gam[n - 1];
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+        f32x4 U = {0.f, 0.f, 0.f, 0.f};
+        const int key = 16 * kt + lr;
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const bf16x8 ka = cat4(*reinterpret_cast<const bf16x4 *>(&sm.Kt[key][32 * p + 4 * lg]),
+                                   *reinterpret_cast<const bf16x4 *>(&sm.Kt[key][32 * p + 16 + 4 * lg]));
+            U = mma(ka, eB[p].hi, U);
+            U = mma(ka, eB[p].lo, U);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st[kt][r] = glast * st[kt][r] + U[r];
+        sched_fence<F>();
+    }
+}
+
+// v[t][irow] for the lane's rows t = 16 tt + 4 lg + r of a chunk (raw bf16 bits;
+// rows past the prompt read the last valid row and are masked at use).
+struct ChunkV {
+    uint16_t raw[4][4];
+    __device__ inline void load(const __hip_bfloat16 *v, size_t row0, int n, int H, int h, int DV,
+                                int irow, int lg) {
+        const uint16_t *vb = reinterpret_cast<const uint16_t *>(v);
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * tt + 4 * lg + r;
+                raw[tt][r] = vb[((row0 + min(t, n - 1)) * H + h) * DV + irow];
+            }
+    }
+    __device__ inline void get(float (&vv)[4][4], int n, int lg) const {
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * tt + 4 * lg + r;
+                vv[tt][r] = t < n ? bf16_bits_to_f32(raw[tt][r]) : 0.f;
+            }
+    }
+};
+
+template <int DK>
+__device__ inline void clear_mats(Smem<DK> &sm, int tid, int nt) {
+    for (int idx = tid; idx < C * (C + 4); idx += nt) {
+        (&sm.Am[0][0])[idx] = 0.f;
+        (&sm.Tm[0][0])[idx] = 0.f;
+        (&sm.Pm[0][0])[idx] = 0.f;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// One pass: one workgroup per (instance, head), NWS waves of 16 value rows.
+// ---------------------------------------------------------------------------
 template <int DK, int DV, int NWS>
 __global__ __launch_bounds__(64 * NWS) void prefill_kernel(
     float *__restrict__ S, const __hip_bfloat16 *__restrict__ q, const __hip_bfloat16 *__restrict__ k,
@@ -86,12 +478,9 @@ __global__ __launch_bounds__(64 * NWS) void prefill_kernel(
     int L, int H, float *__restrict__ o) {
     constexpr int RS = 16 * NWS;       // value rows per workgroup
     constexpr int SLICES = DV / RS;
-    constexpr int KT = DK / 16;        // 16-key tiles
-    constexpr int KB = DK / 32;        // 32-key contraction blocks
+    constexpr int KT = DK / 16;
     constexpr int NT = 64 * NWS;
-    constexpr int NLD = C * DK / 8 / NT;  // 16-byte staging pieces per thread per tensor
-    static_assert(SLICES * RS == DV && KB >= 1, "tiling");
-    static_assert(NLD >= 1 && NLD * NT * 8 == C * DK, "staging tiling");
+    static_assert(SLICES * RS == DV, "tiling");
 
     __shared__ Smem<DK> sm;
 
@@ -102,12 +491,7 @@ __global__ __launch_bounds__(64 * NWS) void prefill_kernel(
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 15, lg = lane >> 4;
     const int irow = slice * RS + w * 16 + lr;  // value row of this lane's column
-
-    for (int idx = tid; idx < C * (C + 4); idx += NT) {
-        (&sm.Am[0][0])[idx] = 0.f;
-        (&sm.Tm[0][0])[idx] = 0.f;
-        (&sm.Pm[0][0])[idx] = 0.f;
-    }
+    clear_mats(sm, tid, NT);
 
     // State slice in registers: st[kt][r] = S[irow][16 kt + 4 lg + r].
     float *Srow = S + (size_t(bh) * DV + irow) * DK;
@@ -126,248 +510,22 @@ __global__ __launch_bounds__(64 * NWS) void prefill_kernel(
         const int c0 = c * C;
         const int n = min(C, L - c0);
         const size_t row0 = size_t(b) * L + c0;  // (b, c0) token row
-
-        // ---- stage the chunk's keys, queries and gates (rows >= n are zero) ----
-        // Every load is issued before any store, so one memory latency covers them.
         {
-            uint4 kv[NLD], qv[NLD];
-#pragma unroll
-            for (int u = 0; u < NLD; ++u) {
-                const int idx = tid + u * NT;
-                const int t = idx / (DK / 8), col = (idx - t * (DK / 8)) * 8;
-                // Clamped rows keep every load valid and branch-free; rows past
-                // the prompt are zeroed after the load.
-                const size_t off = ((row0 + min(t, n - 1)) * H + h) * DK + col;
-                kv[u] = *reinterpret_cast<const uint4 *>(k + off);
-                qv[u] = *reinterpret_cast<const uint4 *>(q + off);
-                if (t >= n) {
-                    kv[u] = make_uint4(0u, 0u, 0u, 0u);
-                    qv[u] = make_uint4(0u, 0u, 0u, 0u);
-                }
-            }
+            ChunkKQ<DK, NT> kq;
+            kq.load(k, q, row0, n, H, h, tid);
             const size_t gi = (row0 + min(lane, n - 1)) * H + h;
-            float gt = g[gi], bt = beta[gi];
-            if (lane >= n) {
-                gt = 0.f;
-                bt = 0.f;
-            }
-#pragma unroll
-            for (int u = 0; u < NLD; ++u) {
-                const int idx = tid + u * NT;
-                const int t = idx / (DK / 8), col = (idx - t * (DK / 8)) * 8;
-                *reinterpret_cast<uint4 *>(&sm.Ks[t][col]) = kv[u];
-                *reinterpret_cast<uint4 *>(&sm.Qs[t][col]) = qv[u];
-                const __bf16 *kh = reinterpret_cast<const __bf16 *>(&kv[u]);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) sm.Kt[col + e][t] = kh[e];
-            }
-            if (w == 0) {
-                float Gp = gt;  // inclusive prefix sum over the chunk
-#pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    const float y = __shfl_up(Gp, off, 64);
-                    if (lane >= off) Gp += y;
-                }
-                const float Glast = __shfl(Gp, n - 1, 64);
-                sm.G[lane] = Gp;
-                sm.gam[lane] = __expf(Gp);
-                sm.ee[lane] = lane < n ? __expf(Glast - Gp) : 0.f;
-                sm.bet[lane] = bt;
-            }
+            const float gt = g[gi], bt = beta[gi];
+            kq.store(sm, n, tid);
+            if (w == 0) chunk_gates(sm, gt, bt, n, lane);
         }
         __syncthreads();
-
-        // ---- Gram tiles: A from K K^T, P from Q K^T (lower tiles only) ----
-        for (int qi = w; qi < 20; qi += NWS) {
-            const bool isq = qi >= 10;
-            const int p = isq ? qi - 10 : qi;
-            const int tt = p >= 6 ? 3 : p >= 3 ? 2 : p >= 1 ? 1 : 0;
-            const int jt = p - tt * (tt + 1) / 2;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                const bf16x8 a = isq ? *reinterpret_cast<const bf16x8 *>(&sm.Qs[16 * tt + lr][32 * kb + 8 * lg])
-                                     : *reinterpret_cast<const bf16x8 *>(&sm.Ks[16 * tt + lr][32 * kb + 8 * lg]);
-                const bf16x8 bk = *reinterpret_cast<const bf16x8 *>(&sm.Ks[16 * jt + lr][32 * kb + 8 * lg]);
-                acc = mma(a, bk, acc);
-            }
-            const int j = 16 * jt + lr;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * tt + 4 * lg + r;
-                const float dec = __expf(sm.G[t] - sm.G[j]);
-                if (isq)
-                    sm.Pm[t][j] = j <= t ? dec * acc[r] : 0.f;
-                else
-                    sm.Am[t][j] = j < t ? sm.bet[t] * dec * acc[r] : 0.f;
-            }
-        }
-        __syncthreads();
-
-        // ---- Linv = (I + A)^{-1}, by 16x16 blocks ----
-        // Diagonal blocks by forward substitution: lane = (block lg, column lr).
-        if (w == 0) {
-            const int base = 16 * lg;
-            float x[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float acc = r == lr ? 1.f : 0.f;
-#pragma unroll
-                for (int jj = 0; jj < r; ++jj) acc -= sm.Am[base + r][base + jj] * x[jj];
-                x[r] = acc;
-                asm volatile("" ::: "memory");  // keep each row's loads with its row (register pressure)
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sm.Tm[base + r][base + lr] = x[r];
-        }
-        __syncthreads();
-        // Off-diagonal blocks, one block diagonal at a time:
-        //   X_ij = -X_ii sum_{m=j}^{i-1} A_im X_mj   (i = j + d).
-        for (int d = 1; d <= 3; ++d) {
-            const int npairs = 4 - d;
-            for (int idx = tid; idx < npairs * 256; idx += NT) {
-                const int j = idx >> 8, r = (idx >> 4) & 15, cc = idx & 15;
-                const int i = j + d;
-                float acc = 0.f;
-                for (int mb = j; mb < i; ++mb)
-#pragma unroll
-                    for (int m = 0; m < 16; ++m)
-                        acc += sm.Am[16 * i + r][16 * mb + m] * sm.Tm[16 * mb + m][16 * j + cc];
-                sm.Wb[j][r][cc] = acc;
-            }
-            __syncthreads();
-            for (int idx = tid; idx < npairs * 256; idx += NT) {
-                const int j = idx >> 8, r = (idx >> 4) & 15, cc = idx & 15;
-                const int i = j + d;
-                float acc = 0.f;
-#pragma unroll
-                for (int m = 0; m < 16; ++m) acc += sm.Tm[16 * i + r][16 * i + m] * sm.Wb[j][m][cc];
-                sm.Tm[16 * i + r][16 * j + cc] = -acc;
-            }
-            __syncthreads();
-        }
-
-        // ---- state-coupled products for this wave's 16 value rows ----
-        // The contraction over keys visits, for block p and lane group lg, keys
-        // 32p + 4lg + {0..3} and 32p + 16 + 4lg + {0..3}: the keys this lane holds
-        // in st[2p] and st[2p+1].
-        float vv[4][4];  // v[t][irow] for t = 16 tt + 4 lg + r
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * tt + 4 * lg + r;
-                const float x = load1(v + ((row0 + min(t, n - 1)) * H + h) * DV + irow);
-                vv[tt][r] = t < n ? x : 0.f;
-            }
-        Split8 sB[KB];
-#pragma unroll
-        for (int p = 0; p < KB; ++p) {
-            const float x[8] = {st[2 * p][0], st[2 * p][1], st[2 * p][2], st[2 * p][3],
-                                st[2 * p + 1][0], st[2 * p + 1][1], st[2 * p + 1][2], st[2 * p + 1][3]};
-            sB[p] = split8(x);
-        }
-        // R = diag(beta) (V - diag(gamma) K S^T), rows t = 16 tt + 4 lg + r.
-        float R[4][4];
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-            f32x4 X = {0.f, 0.f, 0.f, 0.f};
-            const int t = 16 * tt + lr;
-#pragma unroll
-            for (int p = 0; p < KB; ++p) {
-                const bf16x8 ka = cat4(*reinterpret_cast<const bf16x4 *>(&sm.Ks[t][32 * p + 4 * lg]),
-                                       *reinterpret_cast<const bf16x4 *>(&sm.Ks[t][32 * p + 16 + 4 * lg]));
-                X = mma(ka, sB[p].hi, X);
-                X = mma(ka, sB[p].lo, X);
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int tr = 16 * tt + 4 * lg + r;
-                R[tt][r] = sm.bet[tr] * (vv[tt][r] - sm.gam[tr] * X[r]);
-            }
-        }
-        // D = Linv R (Linv is lower triangular: only blocks p <= tt / 2).
-        Split8 rB[2];
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const float x[8] = {R[2 * p][0], R[2 * p][1], R[2 * p][2], R[2 * p][3],
-                                R[2 * p + 1][0], R[2 * p + 1][1], R[2 * p + 1][2], R[2 * p + 1][3]};
-            rB[p] = split8(x);
-        }
-        f32x4 D[4];
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-            D[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const int t = 16 * tt + lr;
-#pragma unroll
-            for (int p = 0; p <= tt / 2; ++p) {
-                const float4 a0 = *reinterpret_cast<const float4 *>(&sm.Tm[t][32 * p + 4 * lg]);
-                const float4 a1 = *reinterpret_cast<const float4 *>(&sm.Tm[t][32 * p + 16 + 4 * lg]);
-                const float x[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-                D[tt] = mma3(split8(x), rB[p], D[tt]);
-            }
-        }
-        // O = diag(gamma) Q S^T + P D.
-        Split8 dB[2];
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const float x[8] = {D[2 * p][0], D[2 * p][1], D[2 * p][2], D[2 * p][3],
-                                D[2 * p + 1][0], D[2 * p + 1][1], D[2 * p + 1][2], D[2 * p + 1][3]};
-            dB[p] = split8(x);
-        }
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-            f32x4 Y = {0.f, 0.f, 0.f, 0.f};
-            const int t = 16 * tt + lr;
-#pragma unroll
-            for (int p = 0; p < KB; ++p) {
-                const bf16x8 qa = cat4(*reinterpret_cast<const bf16x4 *>(&sm.Qs[t][32 * p + 4 * lg]),
-                                       *reinterpret_cast<const bf16x4 *>(&sm.Qs[t][32 * p + 16 + 4 * lg]));
-                Y = mma(qa, sB[p].hi, Y);
-                Y = mma(qa, sB[p].lo, Y);
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Y[r] *= sm.gam[16 * tt + 4 * lg + r];
-#pragma unroll
-            for (int p = 0; p <= tt / 2; ++p) {
-                const float4 a0 = *reinterpret_cast<const float4 *>(&sm.Pm[t][32 * p + 4 * lg]);
-                const float4 a1 = *reinterpret_cast<const float4 *>(&sm.Pm[t][32 * p + 16 + 4 * lg]);
-                const float x[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-                Y = mma3(split8(x), dB[p], Y);
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int tr = 16 * tt + 4 * lg + r;
-                if (tr < n) o[((row0 + tr) * H + h) * DV + irow] = Y[r];
-            }
-        }
-        // S <- gamma_last S + K^T diag(e) D; the result tiles over keys match st[][].
-        Split8 eB[2];
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            float x[8];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                x[e] = sm.ee[32 * p + 4 * lg + e] * D[2 * p][e];
-                x[4 + e] = sm.ee[32 * p + 16 + 4 * lg + e] * D[2 * p + 1][e];
-            }
-            eB[p] = split8(x);
-        }
-        const float glast = sm.gam[n - 1];
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
-            f32x4 U = {0.f, 0.f, 0.f, 0.f};
-            const int key = 16 * kt + lr;
-#pragma unroll
-            for (int p = 0; p < 2; ++p) {
-                const bf16x8 ka = cat4(*reinterpret_cast<const bf16x4 *>(&sm.Kt[key][32 * p + 4 * lg]),
-                                       *reinterpret_cast<const bf16x4 *>(&sm.Kt[key][32 * p + 16 + 4 * lg]));
-                U = mma(ka, eB[p].hi, U);
-                U = mma(ka, eB[p].lo, U);
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) st[kt][r] = glast * st[kt][r] + U[r];
-        }
+        chunk_prep<DK, NWS>(sm, tid, w, lane);
+        split_mats<DK, NT>(sm, tid);
+        ChunkV cv;
+        cv.load(v, row0, n, H, h, DV, irow, lg);
+        float vv[4][4];
+        cv.get(vv, n, lg);
+        chunk_state<DK, true>(sm, st, vv, n, lane, o + (row0 * H + h) * DV + irow, size_t(H) * DV);
         __syncthreads();  // the next chunk overwrites the shared buffers
     }
 
@@ -377,29 +535,208 @@ __global__ __launch_bounds__(64 * NWS) void prefill_kernel(
             make_float4(st[kt][0], st[kt][1], st[kt][2], st[kt][3]);
 }
 
+// ---------------------------------------------------------------------------
+// Two passes, first: one workgroup per (instance, head, chunk) builds Linv, P and
+// the gates of its chunk and writes them to the workspace.
+// ---------------------------------------------------------------------------
+template <int DK>
+__global__ __launch_bounds__(256) void prefill_prep_kernel(
+    const __hip_bfloat16 *__restrict__ q, const __hip_bfloat16 *__restrict__ k,
+    const float *__restrict__ g, const float *__restrict__ beta, int L, int H, int nchunks,
+    float *__restrict__ ws) {
+    constexpr int NWS = 4, NT = 256;
+    __shared__ PrepSmem<DK> sm;
+    const int bh = blockIdx.x / nchunks, c = blockIdx.x - bh * nchunks;
+    const int b = bh / H, h = bh - b * H;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c0 = c * C, n = min(C, L - c0);
+    const size_t row0 = size_t(b) * L + c0;
+    {
+        ChunkKQ<DK, NT> kq;
+        kq.load(k, q, row0, n, H, h, tid);
+        const size_t gi = (row0 + min(lane, n - 1)) * H + h;
+        const float gt = g[gi], bt = beta[gi];
+        kq.template store<false>(sm, n, tid);
+        if (w == 0) chunk_gates(sm, gt, bt, n, lane);
+    }
+    __syncthreads();
+    chunk_prep<DK, NWS>(sm, tid, w, lane);
+    // Linv hi, Linv lo, P hi, P lo as dense bf16 [C][C], then gam, ee, bet.
+    uint8_t *out = reinterpret_cast<uint8_t *>(ws) + (size_t(bh) * nchunks + c) * kPrepBytes;
+    for (int idx = tid; idx < C * C / 8; idx += NT) {
+        const int t = idx / (C / 8), j8 = (idx - t * (C / 8)) * 8;
+        Split8 ls, ps;
+        split_mats8(sm, t, j8, ls, ps);
+        __bf16 *o16 = reinterpret_cast<__bf16 *>(out) + t * C + j8;
+        *reinterpret_cast<bf16x8 *>(o16) = ls.hi;
+        *reinterpret_cast<bf16x8 *>(o16 + C * C) = ls.lo;
+        *reinterpret_cast<bf16x8 *>(o16 + 2 * C * C) = ps.hi;
+        *reinterpret_cast<bf16x8 *>(o16 + 3 * C * C) = ps.lo;
+    }
+    if (tid < C) {
+        float *gout = reinterpret_cast<float *>(out + kPrepMatBytes);
+        gout[tid] = sm.gam[tid];
+        gout[C + tid] = sm.ee[tid];
+        gout[2 * C + tid] = sm.bet[tid];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Two passes, second: one workgroup per (instance, head, RS value rows) walks the
+// chunks; the next chunk's keys, queries, values, Linv, P and gates are loaded
+// into registers while the current chunk is computed.
+// ---------------------------------------------------------------------------
+template <int DK, int NT>
+struct ChunkMats {
+    static constexpr int NM = 4 * C * C / 8 / NT;        // 16-byte pieces of the four bf16 arrays
+    static constexpr int NG = (3 * C / 4 + NT - 1) / NT;  // float4 of gates per thread
+    static_assert(NM >= 1 && NM * NT * 8 == 4 * C * C, "tiling");
+    uint4 mv[NM];
+    float4 gv[NG];
+    __device__ inline void load(const uint8_t *rec, int tid) {
+#pragma unroll
+        for (int u = 0; u < NM; ++u)
+            mv[u] = *reinterpret_cast<const uint4 *>(rec + size_t(tid + u * NT) * 16);
+#pragma unroll
+        for (int u = 0; u < NG; ++u) {
+            const int idx = min(tid + u * NT, 3 * C / 4 - 1);
+            gv[u] = *reinterpret_cast<const float4 *>(rec + kPrepMatBytes + size_t(idx) * 16);
+        }
+    }
+    __device__ inline void store(Smem<DK> &sm, int tid) const {
+#pragma unroll
+        for (int u = 0; u < NM; ++u) {
+            const int e = (tid + u * NT) * 8;               // element index over the 4 arrays
+            const int which = e / (C * C), rem = e - which * C * C;
+            const int t = rem / C, j8 = rem - t * C;
+            __bf16(*dst)[C + 8] = which == 0 ? sm.LiH : which == 1 ? sm.LiL : which == 2 ? sm.PH : sm.PL;
+            *reinterpret_cast<uint4 *>(&dst[t][j8]) = mv[u];
+        }
+#pragma unroll
+        for (int u = 0; u < NG; ++u) {
+            const int idx = min(tid + u * NT, 3 * C / 4 - 1);  // duplicates write equal data
+            const int which = idx / (C / 4), t4 = (idx - which * (C / 4)) * 4;
+            float *dst = which == 0 ? sm.gam : which == 1 ? sm.ee : sm.bet;
+            *reinterpret_cast<float4 *>(dst + t4) = gv[u];
+        }
+    }
+};
+
 template <int DK, int DV, int NWS>
-hipError_t launch_t(float *S, const void *q, const void *k, const void *v, const float *g,
-                    const float *beta, int L, const gdn_shape &s, float *o, hipStream_t st) {
-    constexpr int SLICES = DV / (16 * NWS);
-    const dim3 grid(unsigned(s.B) * unsigned(s.H) * SLICES), block(64 * NWS);
-    hipLaunchKernelGGL((prefill_kernel<DK, DV, NWS>), grid, block, 0, st, S,
-                       static_cast<const __hip_bfloat16 *>(q), static_cast<const __hip_bfloat16 *>(k),
-                       static_cast<const __hip_bfloat16 *>(v), g, beta, L, s.H, o);
+__global__ __launch_bounds__(64 * NWS) void prefill_scan_kernel(
+    float *__restrict__ S, const __hip_bfloat16 *__restrict__ q, const __hip_bfloat16 *__restrict__ k,
+    const __hip_bfloat16 *__restrict__ v, int L, int H, int nchunks, const float *__restrict__ ws,
+    float *__restrict__ o) {
+    constexpr int RS = 16 * NWS;
+    constexpr int SLICES = DV / RS;
+    constexpr int KT = DK / 16;
+    constexpr int NT = 64 * NWS;
+    static_assert(SLICES * RS == DV, "tiling");
+
+    __shared__ Smem<DK> sm;
+
+    const int wg = blockIdx.x;
+    const int bh = wg / SLICES, slice = wg - bh * SLICES;
+    const int b = bh / H, h = bh - b * H;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int irow = slice * RS + w * 16 + lr;
+    const uint8_t *wsh = reinterpret_cast<const uint8_t *>(ws) + size_t(bh) * nchunks * kPrepBytes;
+
+    float *Srow = S + (size_t(bh) * DV + irow) * DK;
+    float st[KT][4];
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+        const float4 s4 = *reinterpret_cast<const float4 *>(Srow + 16 * kt + 4 * lg);
+        st[kt][0] = s4.x;
+        st[kt][1] = s4.y;
+        st[kt][2] = s4.z;
+        st[kt][3] = s4.w;
+    }
+
+    ChunkKQ<DK, NT> kq;
+    ChunkMats<DK, NT> mats;
+    ChunkV cv;
+    {
+        const int n0 = min(C, L);
+        kq.load(k, q, size_t(b) * L, n0, H, h, tid);
+        mats.load(wsh, tid);
+        cv.load(v, size_t(b) * L, n0, H, h, DV, irow, lg);
+    }
+    for (int c = 0; c < nchunks; ++c) {
+        const int c0 = c * C, n = min(C, L - c0);
+        const size_t row0 = size_t(b) * L + c0;
+        kq.store(sm, n, tid);
+        mats.store(sm, tid);
+        float vv[4][4];
+        cv.get(vv, n, lg);
+        __syncthreads();
+        // Prefetch the next chunk (the last chunk again at the end: valid
+        // addresses, no branch).
+        {
+            const int cn = min(c + 1, nchunks - 1), c0n = cn * C, nn = min(C, L - c0n);
+            const size_t row0n = size_t(b) * L + c0n;
+            kq.load(k, q, row0n, nn, H, h, tid);
+            mats.load(wsh + size_t(cn) * kPrepBytes, tid);
+            cv.load(v, row0n, nn, H, h, DV, irow, lg);
+        }
+        chunk_state<DK, false>(sm, st, vv, n, lane, o + (row0 * H + h) * DV + irow, size_t(H) * DV);
+        __syncthreads();  // the next chunk overwrites the shared buffers
+    }
+
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+        *reinterpret_cast<float4 *>(Srow + 16 * kt + 4 * lg) =
+            make_float4(st[kt][0], st[kt][1], st[kt][2], st[kt][3]);
+}
+
+template <int DK, int DV>
+hipError_t launch_dk_dv(float *S, const void *q, const void *k, const void *v, const float *g,
+                        const float *beta, int L, const gdn_shape &s, float *o, void *ws,
+                        size_t ws_bytes, hipStream_t st) {
+    auto *qq = static_cast<const __hip_bfloat16 *>(q);
+    auto *kk = static_cast<const __hip_bfloat16 *>(k);
+    auto *vv = static_cast<const __hip_bfloat16 *>(v);
+    const long heads = long(s.B) * s.H;
+    const int nchunks = (L + C - 1) / C;
+    if (heads < kFewHeads && ws != nullptr && ws_bytes >= size_t(heads) * nchunks * kPrepBytes) {
+        hipLaunchKernelGGL((prefill_prep_kernel<DK>), dim3(unsigned(heads * nchunks)), dim3(256), 0, st,
+                           qq, kk, g, beta, L, s.H, nchunks, static_cast<float *>(ws));
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        constexpr int NWS = 2;  // 32 value rows per workgroup: more compute units on the scan
+        hipLaunchKernelGGL((prefill_scan_kernel<DK, DV, NWS>), dim3(unsigned(heads * (DV / (16 * NWS)))),
+                           dim3(64 * NWS), 0, st, S, qq, kk, vv, L, s.H, nchunks,
+                           static_cast<const float *>(ws), o);
+        return hipGetLastError();
+    }
+    // One pass: one workgroup per head.
+    hipLaunchKernelGGL((prefill_kernel<DK, DV, DV / 16>), dim3(unsigned(heads)), dim3(4 * DV), 0, st,
+                       S, qq, kk, vv, g, beta, L, s.H, o);
     return hipGetLastError();
 }
 
 }  // namespace
 
-// One workgroup per (instance, head): the chunk's shared quantities (Gram
-// matrices, Linv, gates) are built once per head, and each wave owns 16 value rows.
+size_t prefill_workspace_bytes(const gdn_shape &shp, int L) {
+    const long heads = long(shp.B) * shp.H;
+    if (heads >= kFewHeads || L <= 0) return 0;
+    return size_t(heads) * size_t((L + C - 1) / C) * kPrepBytes;
+}
+
 hipError_t launch_prefill(float *S, const void *q, const void *k, const void *v, const float *g,
                           const float *beta, int L, gdn_in_dtype dt, const gdn_shape &shp, float *o,
-                          hipStream_t stream) {
+                          void *ws, size_t ws_bytes, hipStream_t stream) {
     if (dt != GDN_IN_BF16) return hipErrorInvalidValue;
-    if (shp.dk == 128 && shp.dv == 128) return launch_t<128, 128, 8>(S, q, k, v, g, beta, L, shp, o, stream);
-    if (shp.dk == 128 && shp.dv == 64) return launch_t<128, 64, 4>(S, q, k, v, g, beta, L, shp, o, stream);
-    if (shp.dk == 64 && shp.dv == 128) return launch_t<64, 128, 8>(S, q, k, v, g, beta, L, shp, o, stream);
-    return launch_t<64, 64, 4>(S, q, k, v, g, beta, L, shp, o, stream);
+    if (shp.dk == 128 && shp.dv == 128)
+        return launch_dk_dv<128, 128>(S, q, k, v, g, beta, L, shp, o, ws, ws_bytes, stream);
+    if (shp.dk == 128 && shp.dv == 64)
+        return launch_dk_dv<128, 64>(S, q, k, v, g, beta, L, shp, o, ws, ws_bytes, stream);
+    if (shp.dk == 64 && shp.dv == 128)
+        return launch_dk_dv<64, 128>(S, q, k, v, g, beta, L, shp, o, ws, ws_bytes, stream);
+    return launch_dk_dv<64, 64>(S, q, k, v, g, beta, L, shp, o, ws, ws_bytes, stream);
 }
 
 }  // namespace gdn

@@ -181,9 +181,15 @@ def gdn_prefill_workspace_bytes(S, L: int, chunk: int = GDN_PREFILL_CHUNK) -> in
 def gdn_prefill_chunked(S, q, k, v, g, beta, o, chunk: int = GDN_PREFILL_CHUNK, ws=None,
                         stream=None) -> None:
     """Run the prompt (q, k, v, g, beta) through the recurrence: o[:] = all outputs,
-    S advanced in place to the final state."""
+    S advanced in place to the final state.  ``ws`` is the optional workspace of
+    gdn_prefill_workspace_bytes bytes; when None it is allocated here (device
+    memory only; all work runs in libgdn's kernels)."""
     shp = _shape_of(S)
     L = _check_rows(shp, q, k, v, g, beta, o)
+    if ws is None:
+        need = int(lib.gdn_prefill_workspace_bytes(ctypes.byref(shp), L, chunk))
+        if need > 0:
+            ws = torch.empty(need, dtype=torch.uint8, device=S.device)
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     rc = lib.gdn_prefill_chunked(_ptr(S), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), L,
                                  chunk, _dt(q), ctypes.byref(shp), _ptr(o), _ptr(ws), ws_bytes,

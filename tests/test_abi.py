@@ -96,4 +96,9 @@ def test_record_size_accounts_for_payload(G):
         assert n % 256 == 0
     assert G.lib.gdn_block_record_bytes(_shape(), 0, 0) == 0
     assert G.lib.gdn_block_record_bytes(_shape(), 8, 5) == 0
-    assert G.lib.gdn_prefill_workspace_bytes(_shape(), 4096, 64) == 0
+    # Few heads: the two-pass schedule's workspace (Linv, P and gates per chunk).
+    n = G.lib.gdn_prefill_workspace_bytes(_shape(B=1, H=32, dk=128, dv=128), 4096, 64)
+    assert n >= 32 * 64 * (2 * 64 * 64 + 3 * 64) * 4 and n % 256 == 0
+    # Many heads: one pass, no workspace.
+    assert G.lib.gdn_prefill_workspace_bytes(_shape(B=48, H=32, dk=128, dv=128), 4096, 64) == 0
+    assert G.lib.gdn_prefill_workspace_bytes(_shape(), 4096, 32) == 0

@@ -146,3 +146,26 @@ def test_prefill_48_layers_32k_sampled(G):
         assert eo <= OUT_TOL and es <= STATE_TOL
     del x, o, S
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("schedule", ["two_pass", "one_pass"])
+@pytest.mark.parametrize("dk,dv,L", [(128, 128, 300), (64, 128, 129), (128, 64, 64)])
+def test_prefill_both_schedules(G, schedule, dk, dv, L):
+    """Few heads run two passes (parallel chunk prep into the workspace, then the
+    scan) when given the workspace, and one pass without it; both reach the
+    sequential oracle."""
+    B, H = 1, 4
+    print_case(test="prefill_schedules", schedule=schedule, dk=dk, dv=dv, L=L, seed=31)
+    x = make_inputs(B, H, dk, dv, L, seed=31, device=DEV)
+    xc = x.to("cpu")
+    need = G.gdn_prefill_workspace_bytes(x.S0, L)
+    assert need > 0
+    ws = torch.empty(need if schedule == "two_pass" else 0, dtype=torch.uint8, device=DEV)
+    o = torch.full((B, L, H, dv), float("nan"), dtype=torch.float32, device=DEV)
+    S = x.S0.clone()
+    G.gdn_prefill_chunked(S, x.q, x.k, x.v, x.g, x.beta, o, ws=ws)
+    torch.cuda.synchronize()
+    ref_o, ref_S = oracle.prefill_seq(xc.S0, xc.q, xc.k, xc.v, xc.g, xc.beta)
+    assert not torch.isnan(o).any()
+    assert rel_err_outputs(o, ref_o) <= OUT_TOL
+    assert rel_err_state(S, ref_S) <= STATE_TOL
