@@ -52,6 +52,9 @@ def parse():
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="after the bench, run 3 plain device copies of this many MiB (a "
                         "reference kernel of known traffic for hardware counters)")
+    p.add_argument("--summarize", metavar="DIR", default=None,
+                   help="no GPU work: turn the rocprofv3 outputs under DIR (stats/, fetch/, "
+                        "write/ and commands.txt) into the summaries under profiles/")
     return p.parse_args()
 
 
@@ -96,10 +99,14 @@ def sources_hash():
     return h.hexdigest()[:16]
 
 
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "hbm_traffic_verify_commit_48x32_T8_prefill_32x4096.json")
+STATS_MD = os.path.join(ROOT, "profiles", "kernel_stats_verify_commit_48x32_T8_prefill_32x4096.md")
+
+
 def load_traffic(kernel):
     """HBM bytes per launch from the committed rocprofv3 counter summary, only if
     it was taken on the current kernel sources."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+    path = TRAFFIC_JSON
     try:
         with open(path) as f:
             t = json.load(f)
@@ -109,6 +116,63 @@ def load_traffic(kernel):
         return None
     k = t.get("kernels", {}).get(kernel)
     return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def accept_count(args):
+    """Passes whose accepted lengths are drawn: warmup, the headline region and
+    the kernel-timing region."""
+    return args.warmup + 2 * args.steps
+
+
+class KernelEvents:
+    """Timing events on the launch stream.  HIP events created with
+    hipEventDisableSystemFence: an event without the flag releases to system
+    scope when it completes, which adds a few microseconds to the interval
+    around a 30 us kernel.  Falls back to torch's events if the HIP runtime
+    cannot be reached."""
+
+    def __init__(self, torch, stream):
+        import ctypes
+
+        self.ctypes, self.torch = ctypes, torch
+        self.stream = ctypes.c_void_p(stream.cuda_stream)
+        try:
+            self.hip = ctypes.CDLL("libamdhip64.so.7")
+            e = self._create()
+            self.hip.hipEventDestroy(e)
+            self.kind = "hipEvent, hipEventDisableSystemFence"
+        except (OSError, RuntimeError):
+            self.hip = None
+            self.kind = "torch.cuda.Event"
+
+    def _create(self):
+        e = self.ctypes.c_void_p()
+        if self.hip.hipEventCreateWithFlags(self.ctypes.byref(e), self.ctypes.c_uint(0x20000000)) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        return e
+
+    def new(self):
+        return self._create() if self.hip else self.torch.cuda.Event(enable_timing=True)
+
+    def record(self, e):
+        if self.hip:
+            if self.hip.hipEventRecord(e, self.stream) != 0:
+                raise RuntimeError("hipEventRecord failed")
+        else:
+            e.record()
+
+    def ms(self, a, b):
+        if not self.hip:
+            return a.elapsed_time(b)
+        f = self.ctypes.c_float()
+        if self.hip.hipEventElapsedTime(self.ctypes.byref(f), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return f.value
+
+    def free(self, evs):
+        if self.hip:
+            for e in evs:
+                self.hip.hipEventDestroy(e)
 
 
 def cpu_baseline(args):
@@ -141,6 +205,9 @@ def cpu_baseline(args):
 
 def main():
     args = parse()
+    if args.summarize:
+        summarize_profiles(args)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the GDN path is "
               f"single-GPU by design and has no multi-GPU mode.", file=sys.stderr)
@@ -164,7 +231,7 @@ def main():
         o = torch.empty(LAYERS, T, HEADS, DV, dtype=torch.float32, device=dev)
         rec = G.new_record(x.S0, T, dt)
         sets.append((x, o, rec))
-    total = args.warmup + args.steps
+    total = accept_count(args)
     n_host = make_accepts(total, T, seed=args.seed)
     n_dev = n_host.view(total, 1).expand(total, LAYERS).contiguous().to(dev)
     pos = torch.zeros(LAYERS, dtype=torch.int32, device=dev)
@@ -182,37 +249,47 @@ def main():
     for p in range(LAG):
         verify(p)
 
-    def step(s, evs=None):
+    def step(s, kev=None, evs=None):
         if evs is not None:
-            evs[0].record()
+            kev.record(evs[0])
         verify(s + LAG)
         if evs is not None:
-            evs[1].record()
+            kev.record(evs[1])
         commit(s)
         if evs is not None:
-            evs[2].record()
+            kev.record(evs[2])
 
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
 
-    # Timed region: exactly `steps` passes, events on the launch stream.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
+    # Headline region: exactly `steps` passes back to back, nothing between the
+    # launches, wall clock around device synchronisations.
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+        step(args.warmup + i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-
-    n_timed = [int(v) for v in n_host[args.warmup:total]]
+    n_timed = [int(v) for v in n_host[args.warmup:args.warmup + args.steps]]
     tokens = sum(n_timed)
-    t_ver = [evs[i][0].elapsed_time(evs[i][1]) for i in range(args.steps)]
-    t_com = [evs[i][1].elapsed_time(evs[i][2]) for i in range(args.steps)]
+
+    # Kernel-timing region: the next `steps` passes with events on the launch
+    # stream around each kernel (the events add a little time of their own, so
+    # these per-launch averages are upper bounds on the kernels' durations).
+    kev = KernelEvents(torch, torch.cuda.current_stream())
+    evs = [[kev.new() for _ in range(3)] for _ in range(args.steps)]
+    s1 = args.warmup + args.steps
+    for i in range(args.steps):
+        step(s1 + i, kev, evs[i])
+    torch.cuda.synchronize()
+    t_ver = [kev.ms(evs[i][0], evs[i][1]) for i in range(args.steps)]
+    t_com = [kev.ms(evs[i][1], evs[i][2]) for i in range(args.steps)]
+    kev.free([e for ev in evs for e in ev])
+    n_kt = [int(v) for v in n_host[s1:s1 + args.steps]]
     avg_ver_ms = sum(t_ver) / len(t_ver)
     avg_com_ms = sum(t_com) / len(t_com)
     vb = verify_bytes(LAYERS, HEADS, DK, DV, T, es)
-    cb_avg = sum(commit_bytes(LAYERS, HEADS, DK, DV, n, es) for n in n_timed) / len(n_timed)
+    cb_avg = sum(commit_bytes(LAYERS, HEADS, DK, DV, n, es) for n in n_kt) / len(n_kt)
     ver_gbs = vb / (avg_ver_ms * 1e-3) / 1e9
     com_gbs = cb_avg / (avg_com_ms * 1e-3) / 1e9
     pass_gbs = (vb + cb_avg) / ((avg_ver_ms + avg_com_ms) * 1e-3) / 1e9
@@ -249,10 +326,12 @@ def main():
                    "input_dtype": "bf16", "tokens_committed": tokens},
         "rows_per_s": round(T * args.steps / wall, 1),
         "pass_hbm_frac": round(pass_gbs / HBM_PEAK_GBS, 4),
+        "kernel_timing": {"events": kev.kind, "region": f"{args.steps} passes after the headline region"},
         "roofline": roof,
         "kernels": kernels,
     }
 
+    result["copy_ceiling"] = copy_ceiling(dev)
     if not args.no_prefill:
         result["prefill"] = bench_prefill(args, G, dev)
     if not args.no_cpu_baseline:
@@ -268,6 +347,148 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+def copy_ceiling(dev, mib=1024, reps=10):
+    """Achieved GB/s of a plain device-to-device copy (bytes read + written): the
+    practical HBM ceiling on this device, reported beside the peak for context."""
+    import torch
+
+    src = torch.ones(mib << 18, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    gbs = 2 * src.numel() * 4 * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"kernel": "torch copy_", "mib": mib, "achieved": round(gbs, 1), "unit": "GB/s",
+            "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def _read_csv(pattern):
+    import csv
+    import glob
+
+    paths = sorted(glob.glob(pattern, recursive=True))
+    if not paths:
+        raise SystemExit(f"no file matches {pattern}")
+    with open(paths[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_profiles(args):
+    """Write the profile summaries from one directory of rocprofv3 output:
+      stats/**/*kernel_stats.csv            --kernel-trace --stats run of bench.py
+      fetch/**/*counter_collection.csv      --pmc FETCH_SIZE run
+      write/**/*counter_collection.csv      --pmc WRITE_SIZE run (same command)
+      commands.txt                          the three commands, one a line
+    The counter runs must use --copy-calibration-mib; the copy's bytes scale the
+    raw counters (per dispatch, KiB) to bytes.  --steps/--warmup/--seed must be
+    those of the counter runs: the commit's accepted lengths, and so its
+    algorithmic bytes, follow from them."""
+    from speculative_verify_amd.inputs import make_accepts
+
+    d = args.summarize
+    with open(os.path.join(d, "commands.txt")) as f:
+        commands = [ln.rstrip("\n") for ln in f if ln.strip()]
+
+    # Kernel-trace statistics.
+    stats = _read_csv(os.path.join(d, "stats", "**", "*kernel_stats.csv"))
+    lines = ["# Kernel time: verify + commit (48 layers x 32 heads, d=128, T=8) and chunked "
+             "prefill (32 heads, L=4096)", "",
+             "rocprofv3 `--kernel-trace --stats` of the benchmark, GPU kernels of libgdn only "
+             "(torch's input generation and copies omitted).", "", "Command:", "", "```",
+             commands[0], "```", "", "| kernel | calls | average us | min us | max us | share of listed time |",
+             "|---|---|---|---|---|---|"]
+    rows = [r for r in stats if "gdn::" in r["Name"]]
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        name = r["Name"].replace("void gdn::(anonymous namespace)::", "").split("(")[0]
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['TotalDurationNs']) / total:.3f} |")
+    with open(STATS_MD, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    # Hardware counters: FETCH_SIZE and WRITE_SIZE per dispatch (KiB), scaled by
+    # what they read for a plain copy of known size.
+    def per_dispatch(sub):
+        out = {}
+        for r in _read_csv(os.path.join(d, sub, "**", "*counter_collection.csv")):
+            key = int(r["Dispatch_Id"])
+            e = out.setdefault(key, {"name": r["Kernel_Name"], "grid": int(r["Grid_Size"]), "kib": 0.0})
+            e["kib"] += float(r["Counter_Value"])
+        return out
+
+    fetch, write = per_dispatch("fetch"), per_dispatch("write")
+    calib_kib = None
+    for c in commands:
+        if "--copy-calibration-mib" in c:
+            calib_kib = int(c.split("--copy-calibration-mib")[1].split()[0]) * 1024
+    if calib_kib is None:
+        raise SystemExit("the counter runs need --copy-calibration-mib")
+    # The calibration copies are the dispatches whose WRITE_SIZE is the copy's size.
+    cal = [k for k, e in write.items() if "copyBuffer" in e["name"] and abs(e["kib"] - calib_kib) < 0.02 * calib_kib]
+    cal = [k for k in cal if k in fetch and fetch[k]["grid"] == write[k]["grid"]]
+    if not cal:
+        raise SystemExit("calibration copy dispatches not found")
+    fetch_factor = calib_kib / (sum(fetch[k]["kib"] for k in cal) / len(cal))
+    write_factor = calib_kib / (sum(write[k]["kib"] for k in cal) / len(cal))
+
+    def kernel_rows(tag):
+        ids = sorted(k for k, e in fetch.items() if tag in e["name"] and k in write)
+        return [(k, fetch[k]["kib"] * 1024 * fetch_factor, write[k]["kib"] * 1024 * write_factor) for k in ids]
+
+    es = 2
+    summary = {"sources_sha256_16": sources_hash(), "commands": commands,
+               "calibration": {"copy_kib": calib_kib, "dispatches": len(cal),
+                               "fetch_factor": round(fetch_factor, 4), "write_factor": round(write_factor, 4)},
+               "kernels": {}}
+    ver = kernel_rows("verify_kernel")
+    if ver:
+        vb = verify_bytes(LAYERS, HEADS, DK, DV, T, es)
+        fr = sum(r[1] for r in ver) / len(ver)
+        wr = sum(r[2] for r in ver) / len(ver)
+        summary["kernels"]["verify_kernel"] = {
+            "dispatches": len(ver), "read_bytes": round(fr), "write_bytes": round(wr),
+            "hbm_bytes_per_launch": round(fr + wr), "algorithmic_bytes_per_launch": vb,
+            "traffic_over_algorithmic": round((fr + wr) / vb, 3)}
+    com = kernel_rows("commit_kernel")
+    if com:
+        total = accept_count(args)
+        n_host = [int(v) for v in make_accepts(total, T, seed=args.seed)]
+        alg = [commit_bytes(LAYERS, HEADS, DK, DV, n_host[i], es) for i in range(min(len(com), total))]
+        com = com[:len(alg)]
+        fr = sum(r[1] for r in com) / len(com)
+        wr = sum(r[2] for r in com) / len(com)
+        ab = sum(alg) / len(alg)
+        summary["kernels"]["commit_kernel"] = {
+            "dispatches": len(com), "read_bytes": round(fr), "write_bytes": round(wr),
+            "hbm_bytes_per_launch": round(fr + wr), "algorithmic_bytes_per_launch": round(ab),
+            "traffic_over_algorithmic": round((fr + wr) / ab, 3)}
+    # Prefill: every call launches either prefill_kernel or prep + scan; per call.
+    pk = kernel_rows("prefill_kernel<")
+    pp = kernel_rows("prefill_prep_kernel")
+    ps = kernel_rows("prefill_scan_kernel")
+    calls = len(ps) if ps else len(pk)
+    if calls:
+        fr = (sum(r[1] for r in pk + pp + ps)) / calls
+        wr = (sum(r[2] for r in pk + pp + ps)) / calls
+        pb = prefill_bytes(PF_B, PF_H, DK, DV, PF_L)
+        summary["kernels"]["prefill"] = {
+            "calls": calls, "kernels": sorted({e["name"].replace("void gdn::(anonymous namespace)::", "").split("(")[0]
+                                               for k, e in fetch.items() if "prefill" in e["name"]}),
+            "read_bytes": round(fr), "write_bytes": round(wr), "hbm_bytes_per_launch": round(fr + wr),
+            "algorithmic_bytes_per_launch": pb, "traffic_over_algorithmic": round((fr + wr) / pb, 3)}
+    with open(TRAFFIC_JSON, "w") as f:
+        json.dump(summary, f, indent=1)
+        f.write("\n")
+    print(f"wrote {STATS_MD} and {TRAFFIC_JSON}")
+
+
 def bench_prefill(args, G, dev):
     import torch
 
@@ -276,8 +497,10 @@ def bench_prefill(args, G, dev):
     x = make_inputs(PF_B, PF_H, DK, DV, PF_L, seed=args.seed + 77, device=dev, device_gen=True)
     o = torch.empty(PF_B, PF_L, PF_H, DV, dtype=torch.float32, device=dev)
     S = x.S0.clone()
+    need = G.gdn_prefill_workspace_bytes(S, PF_L, PF_C)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev) if need else None
     try:
-        G.gdn_prefill_chunked(S, x.q, x.k, x.v, x.g, x.beta, o)
+        G.gdn_prefill_chunked(S, x.q, x.k, x.v, x.g, x.beta, o, chunk=PF_C, ws=ws)
     except G.GdnError as e:
         return {"status": f"unavailable: {e}"}
     # A 512 MiB buffer rewritten between reps pushes the prompt out of the caches.
@@ -288,7 +511,7 @@ def bench_prefill(args, G, dev):
         S.copy_(x.S0)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
-        G.gdn_prefill_chunked(S, x.q, x.k, x.v, x.g, x.beta, o)
+        G.gdn_prefill_chunked(S, x.q, x.k, x.v, x.g, x.beta, o, chunk=PF_C, ws=ws)
         b.record()
         torch.cuda.synchronize()
         t_ms.append(a.elapsed_time(b))
@@ -299,13 +522,15 @@ def bench_prefill(args, G, dev):
     gbs = by / (avg * 1e-3) / 1e9
     return {"workload": f"chunked prefill: {PF_B} layer x {PF_H} heads, dk=dv={DK}, L={PF_L}, chunk {PF_C}, "
                         f"bf16 in, fp32 state, cold caches",
+            "schedule": "two-pass (chunk prep, then scan)" if need else "one-pass",
+            "workspace_bytes": need,
             "tokens_per_s": round(PF_L / (avg * 1e-3), 1), "avg_launch_us": round(avg * 1e3, 2),
             "mfma": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
                      "flops_per_launch": fl, "flop_convention": "causal"},
             "hbm": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_launch": by,
-                    "traffic": load_traffic("prefill_kernel")}}
+                    "traffic": load_traffic("prefill")}}
 
 
 if __name__ == "__main__":

@@ -636,8 +636,20 @@ __global__ __launch_bounds__(64 * NWS) void prefill_scan_kernel(
 
     __shared__ Smem<DK> sm;
 
-    const int wg = blockIdx.x;
-    const int bh = wg / SLICES, slice = wg - bh * SLICES;
+    // Workgroup i runs on XCD i % 8.  The SLICES workgroups of one head read the
+    // same keys, queries and chunk matrices, so they are placed on one XCD, where
+    // its L2 serves the repeats: within each group of 8 SLICES workgroups, XCD x
+    // takes head 8 g + x, slice = position / 8.  A ragged last group maps linearly.
+    const int wg = blockIdx.x, grp = 8 * SLICES;
+    int bh, slice;
+    if (wg < int(gridDim.x) / grp * grp) {
+        const int g0 = wg / grp, r = wg - g0 * grp;
+        bh = 8 * g0 + (r & 7);
+        slice = r >> 3;
+    } else {
+        bh = wg / SLICES;
+        slice = wg - bh * SLICES;
+    }
     const int b = bh / H, h = bh - b * H;
     const int tid = threadIdx.x, lane = tid & 63;
     const int lr = lane & 15, lg = lane >> 4;

@@ -18,10 +18,13 @@
 //   o_t     = gamma_t S q_t + sum_{j<=t} Gamma_tj (q_t.k_j) delta_j
 //
 // so the state enters only through the 2T projections [K;Q] S^T, one dense
-// (2T x dk) x (dk x dv) contraction per head.  That contraction runs on fp32
-// MFMA (v_mfma_f32_16x16x4_f32): products are exact fp32 products, so no split
-// of the fp32 state is needed, and the VALU is left with O(T^2) work per value
-// row.  The key Gram matrix [K;Q] K^T rides along in the same loop.
+// (2T x dk) x (dk x dv) contraction per head, on MFMA; the VALU is left with
+// O(T^2) work per value row.  For bf16 inputs the rows of [K;Q] are exact bf16
+// operands and the fp32 state is split into a high and a low bf16 part (two
+// v_mfma_f32_16x16x32_bf16 per 32 keys; the dropped residual is below 2^-17 of
+// each state element).  For fp32 inputs the contraction runs on fp32 MFMA
+// (v_mfma_f32_16x16x4_f32).  The Gram matrix [K;Q] K^T is built the same way
+// while the state is still arriving.
 #include "gdn_internal.h"
 
 namespace gdn {
