@@ -327,6 +327,7 @@ def main():
         "rows_per_s": round(T * args.steps / wall, 1),
         "pass_hbm_frac": round(pass_gbs / HBM_PEAK_GBS, 4),
         "kernel_timing": {"events": kev.kind, "region": f"{args.steps} passes after the headline region"},
+        "sources_sha256_16": sources_hash(),
         "roofline": roof,
         "kernels": kernels,
     }
@@ -443,7 +444,15 @@ def summarize_profiles(args):
         return [(k, fetch[k]["kib"] * 1024 * fetch_factor, write[k]["kib"] * 1024 * write_factor) for k in ids]
 
     es = 2
-    summary = {"sources_sha256_16": sources_hash(), "commands": commands,
+    # The kernel sources the counter runs measured: their own bench output names
+    # them; fall back to the tree's sources if that output is missing.
+    src_hash = sources_hash()
+    try:
+        with open(os.path.join(d, "fetch.json")) as f:
+            src_hash = json.loads(f.read().strip().splitlines()[-1]).get("sources_sha256_16", src_hash)
+    except (OSError, ValueError, IndexError):
+        pass
+    summary = {"sources_sha256_16": src_hash, "commands": commands,
                "calibration": {"copy_kib": calib_kib, "dispatches": len(cal),
                                "fetch_factor": round(fetch_factor, 4), "write_factor": round(write_factor, 4)},
                "kernels": {}}

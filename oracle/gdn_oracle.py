@@ -31,11 +31,27 @@ def build(force: bool = True) -> str:
     """Compile the oracle with gcc (OpenMP, strict IEEE: no fast-math)."""
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp"
-        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
-               "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp, "-lm"]
+        cmd = ["gcc", *compile_flags(), _SRC, "-o", tmp, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB)
     return _LIB
+
+
+def compile_flags() -> list[str]:
+    return ["-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-fno-fast-math", "-ffp-contract=off"]
+
+
+def bind(lib: ctypes.CDLL) -> ctypes.CDLL:
+    """Declare the C entry points' signatures on a loaded oracle library."""
+    dp = ctypes.POINTER(ctypes.c_double)
+    ip = ctypes.POINTER(ctypes.c_int)
+    lib.oracle_gdn_seq.restype = ctypes.c_int
+    lib.oracle_gdn_seq.argtypes = [ctypes.c_int] * 5 + [dp] * 6 + [ip, dp, dp]
+    lib.oracle_gdn_chunked.restype = ctypes.c_int
+    lib.oracle_gdn_chunked.argtypes = [ctypes.c_int] * 6 + [dp] * 7
+    lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+    return lib
 
 
 def _load():
@@ -43,16 +59,7 @@ def _load():
     if _lib is None:
         if not os.path.exists(_LIB):
             build(force=False)
-        lib = ctypes.CDLL(_LIB)
-        dp = ctypes.POINTER(ctypes.c_double)
-        ip = ctypes.POINTER(ctypes.c_int)
-        lib.oracle_gdn_seq.restype = ctypes.c_int
-        lib.oracle_gdn_seq.argtypes = [ctypes.c_int] * 5 + [dp] * 6 + [ip, dp, dp]
-        lib.oracle_gdn_chunked.restype = ctypes.c_int
-        lib.oracle_gdn_chunked.argtypes = [ctypes.c_int] * 6 + [dp] * 7
-        lib.oracle_num_threads.restype = ctypes.c_int
-        lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
-        _lib = lib
+        _lib = bind(ctypes.CDLL(_LIB))
     return _lib
 
 

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import oracle
-from speculative_verify_amd.inputs import make_inputs
+from speculative_verify_amd.inputs import make_accepts, make_inputs
 from tests._metrics import OUT_TOL, STATE_TOL, rel_err_outputs, rel_err_state
 
 pytestmark = pytest.mark.gpu
@@ -125,26 +125,59 @@ def test_prefill_rejects_fp32_inputs(G):
         G.gdn_prefill_chunked(x.S0, x.q, x.k, x.v, x.g, x.beta, o)
 
 
-def test_prefill_48_layers_32k_sampled(G):
-    """48 layers x 32 heads, d = 128, a 32,768-token prompt in one launch; the
-    outputs and final state of sampled (layer, head) pairs against the
-    sequential oracle run over the whole prompt."""
-    B, H, d, L = 48, 32, 128, 32768
-    print_case(test="prefill_48x32k", B=B, H=H, d=d, L=L, seed=8)
+def test_prefill_48_layers_32k_then_256_rounds(G):
+    """Long context: 48 layers x 32 heads, d = 128, a 32,768-token prompt in one
+    launch, then 256 speculative rounds (T = 8 verify, commit at n ~ U{0..8},
+    one n per round for all layers) on the prefilled state.  Sampled (layer,
+    head) pairs against the oracle: the prompt's outputs and final state, every
+    round's outputs, and the state after the last round."""
+    B, H, d, L, T, R = 48, 32, 128, 32768, 8, 256
+    print_case(test="prefill_48x32k_rounds", B=B, H=H, d=d, L=L, rounds=R, seed=8)
     x = make_inputs(B, H, d, d, L, seed=8, device=DEV, device_gen=True)
     o = torch.empty(B, L, H, d, dtype=torch.float32, device=DEV)
     S = x.S0.clone()
     G.gdn_prefill_chunked(S, x.q, x.k, x.v, x.g, x.beta, o)
     torch.cuda.synchronize()
-    for (b, h) in [(0, 0), (17, 31), (47, 5)]:
+    picks = [(0, 0), (17, 31), (47, 5)]
+    ref_state = {}
+    for (b, h) in picks:
         pick = lambda a: a[b:b + 1, :, h:h + 1].contiguous().cpu()
         ref_o, ref_S = oracle.prefill_seq(x.S0[b:b + 1, h:h + 1].cpu(), pick(x.q), pick(x.k),
                                           pick(x.v), pick(x.g), pick(x.beta))
         eo = rel_err_outputs(o[b:b + 1, :, h:h + 1], ref_o)
         es = rel_err_state(S[b:b + 1, h:h + 1], ref_S)
-        print(f"  (b={b}, h={h}): out {eo:.3e} state {es:.3e}", flush=True)
+        print(f"  prefill (b={b}, h={h}): out {eo:.3e} state {es:.3e}", flush=True)
         assert eo <= OUT_TOL and es <= STATE_TOL
-    del x, o, S
+        ref_state[(b, h)] = ref_S
+    del x, o
+    torch.cuda.empty_cache()
+
+    # 256 rounds on the prefilled state.
+    y = make_inputs(B, H, d, d, R * T, seed=9, device=DEV, device_gen=True)
+    ns = make_accepts(R, T, seed=9)
+    rec = G.new_record(S, T, torch.bfloat16)
+    ob = torch.empty(B, T, H, d, dtype=torch.float32, device=DEV)
+    pos = torch.zeros(B, dtype=torch.int32, device=DEV)
+    got = {p: [] for p in picks}
+    for r in range(R):
+        blk = lambda a: a[:, r * T:(r + 1) * T].contiguous()
+        G.gdn_verify_block(S, blk(y.q), blk(y.k), blk(y.v), blk(y.g), blk(y.beta), ob, rec)
+        G.gdn_commit(S, rec, torch.full((B,), int(ns[r]), dtype=torch.int32, device=DEV), pos)
+        for (b, h) in picks:
+            got[(b, h)].append(ob[b:b + 1, :, h:h + 1].cpu())
+    torch.cuda.synchronize()
+    assert pos.tolist() == [int(ns.sum())] * B
+    for (b, h) in picks:
+        S_ref, worst = ref_state[(b, h)], 0.0
+        for r in range(R):
+            blk = lambda a: a[b:b + 1, r * T:(r + 1) * T, h:h + 1].contiguous().cpu()
+            args = (blk(y.q), blk(y.k), blk(y.v), blk(y.g), blk(y.beta))
+            worst = max(worst, rel_err_outputs(got[(b, h)][r], oracle.verify(S_ref, *args)))
+            S_ref = oracle.commit(S_ref, *args, np.array([int(ns[r])], np.int32))
+        es = rel_err_state(S[b:b + 1, h:h + 1], S_ref)
+        print(f"  rounds (b={b}, h={h}): worst round out {worst:.3e} final state {es:.3e}", flush=True)
+        assert worst <= OUT_TOL and es <= STATE_TOL
+    del y, S
     torch.cuda.empty_cache()
 
 
