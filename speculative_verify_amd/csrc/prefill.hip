@@ -583,58 +583,233 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Two passes, second: one workgroup per (instance, head, RS value rows) walks the
-// chunks; the next chunk's keys, queries, values, Linv, P and gates are loaded
-// into registers while the current chunk is computed.
+// Two passes, second: one workgroup per (instance, head, 32 value rows) walks
+// the chunks doing only the state-coupled products.  Each chunk's operands
+// (keys, queries, Linv and P split, the gates, the workgroup's value columns)
+// are copied global -> LDS asynchronously one chunk ahead, into the other half
+// of a double buffer, so the walk waits on memory once per chunk at most.
 // ---------------------------------------------------------------------------
-template <int DK, int NT>
-struct ChunkMats {
-    static constexpr int NM = 4 * C * C / 8 / NT;        // 16-byte pieces of the four bf16 arrays
-    static constexpr int NG = (3 * C / 4 + NT - 1) / NT;  // float4 of gates per thread
-    static_assert(NM >= 1 && NM * NT * 8 == 4 * C * C, "tiling");
-    uint4 mv[NM];
-    float4 gv[NG];
-    __device__ inline void load(const uint8_t *rec, int tid) {
-#pragma unroll
-        for (int u = 0; u < NM; ++u)
-            mv[u] = *reinterpret_cast<const uint4 *>(rec + size_t(tid + u * NT) * 16);
-#pragma unroll
-        for (int u = 0; u < NG; ++u) {
-            const int idx = min(tid + u * NT, 3 * C / 4 - 1);
-            gv[u] = *reinterpret_cast<const float4 *>(rec + kPrepMatBytes + size_t(idx) * 16);
-        }
-    }
-    __device__ inline void store(Smem<DK> &sm, int tid) const {
-#pragma unroll
-        for (int u = 0; u < NM; ++u) {
-            const int e = (tid + u * NT) * 8;               // element index over the 4 arrays
-            const int which = e / (C * C), rem = e - which * C * C;
-            const int t = rem / C, j8 = rem - t * C;
-            __bf16(*dst)[C + 8] = which == 0 ? sm.LiH : which == 1 ? sm.LiL : which == 2 ? sm.PH : sm.PL;
-            *reinterpret_cast<uint4 *>(&dst[t][j8]) = mv[u];
-        }
-#pragma unroll
-        for (int u = 0; u < NG; ++u) {
-            const int idx = min(tid + u * NT, 3 * C / 4 - 1);  // duplicates write equal data
-            const int which = idx / (C / 4), t4 = (idx - which * (C / 4)) * 4;
-            float *dst = which == 0 ? sm.gam : which == 1 ? sm.ee : sm.bet;
-            *reinterpret_cast<float4 *>(dst + t4) = gv[u];
-        }
-    }
+
+// global_load_lds_dwordx4: lane l's 16 bytes from `src` land at LDS byte
+// lds_base + 16 l (each lane gathers from its own address).  Issued through
+// inline asm so that the compiler, which cannot count these copies precisely,
+// does not wait for all of them before every LDS read; the scan waits for them
+// itself (vmcnt) at the top of each chunk.
+__device__ inline void dma16(const void *src, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(src)
+                 : "memory", "m0");
+}
+
+__device__ inline uint32_t lds_addr(const void *p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void *)p));
+}
+
+// LDS layouts.  Rows of keys/queries (256 B at dk = 128, 128 B at dk = 64) and
+// of the [C][C] matrices (128 B) keep their 16-byte pieces in an XOR-swizzled
+// order, slot = piece ^ swz(row), so that both the row reads of the MFMA A
+// operands (16 consecutive rows, one piece each) and the transposed reads of
+// the state update (4 consecutive rows, 4 half-pieces) hit distinct banks.
+__device__ inline int swz16(int t) { return ((t & 3) << 2) | ((t >> 2) & 3); }  // 16 pieces a row
+__device__ inline int swz8(int t) {                                               // 8 pieces a row
+    const int y = (t >> 1) & 7;
+    return ((y & 1) << 1) | ((y >> 1) & 1) | (y & 4);
+}
+template <int DK>
+__device__ inline int kq_off(int t, int piece) {  // byte offset of a key/query piece
+    if constexpr (DK == 128)
+        return t * 256 + ((piece ^ swz16(t)) << 4);
+    else
+        return t * 128 + ((piece ^ swz8(t)) << 4);
+}
+__device__ inline int mat_off(int arr, int t, int piece) {  // byte offset in the matrices
+    return arr * (C * C * 2) + t * 128 + ((piece ^ swz8(t)) << 4);
+}
+
+template <int DK>
+struct alignas(16) ScanLds {
+    uint8_t K[2][C * DK * 2];
+    uint8_t Q[2][C * DK * 2];
+    uint8_t M[2][4 * C * C * 2];   // Linv hi, Linv lo, P hi, P lo
+    uint8_t V[2][C * 32 * 2];      // the workgroup's 32 value columns, [t][32] bf16
+    float G[2][256];               // gamma, e, beta (3 x 64), padded to 1 KiB
+    float O[C][32];                // output staging, wave w owns columns 16w .. 16w + 15
 };
 
-template <int DK, int DV, int NWS>
-__global__ __launch_bounds__(64 * NWS) void prefill_scan_kernel(
+typedef short v4s __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
+// i % 4 of the 8 bytes addressed by lane 4 e + i / 4, for e = 0..3.  With lane
+// j addressing row r0 + j / 4, columns c0 + 4 (j % 4) .. + 3 of a row-major
+// 16-bit matrix, lane i receives rows r0 .. r0 + 3 of column c0 + i.
+__device__ inline bf16x4 read_tr(const uint8_t *p) {
+    const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)p);
+    return __builtin_bit_cast(bf16x4, r);
+}
+
+// A operand of a 16-row tile from a swizzled row layout: row t, columns
+// (contraction slots) 32p + 4lg + {0..3} and 32p + 16 + 4lg + {0..3}.
+template <int DK>
+__device__ inline bf16x8 kq_row8(const uint8_t *base, int t, int p, int lg) {
+    const int h8 = (lg & 1) << 3;
+    return cat4(*reinterpret_cast<const bf16x4 *>(base + kq_off<DK>(t, 4 * p + (lg >> 1)) + h8),
+                *reinterpret_cast<const bf16x4 *>(base + kq_off<DK>(t, 4 * p + 2 + (lg >> 1)) + h8));
+}
+__device__ inline bf16x8 mat_row8(const uint8_t *base, int arr, int t, int p, int lg) {
+    const int h8 = (lg & 1) << 3;
+    return cat4(*reinterpret_cast<const bf16x4 *>(base + mat_off(arr, t, 4 * p + (lg >> 1)) + h8),
+                *reinterpret_cast<const bf16x4 *>(base + mat_off(arr, t, 4 * p + 2 + (lg >> 1)) + h8));
+}
+
+// State-coupled products of one chunk for one wave's 16 value rows, from stage
+// s of the LDS buffers (the same products as chunk_state).  obase points at o
+// for the chunk's first token and the workgroup's first value column; ostride
+// is one token.
+template <int DK>
+__device__ inline void scan_chunk(ScanLds<DK> &sm, int s, float (&st)[DK / 16][4], int n, int lane, int w,
+                                  float *__restrict__ obase, size_t ostride) {
+    constexpr int KT = DK / 16, KB = DK / 32;
+    const int lr = lane & 15, lg = lane >> 4;
+    const uint8_t *Kc = sm.K[s], *Qc = sm.Q[s], *Mc = sm.M[s];
+    const float *Gc = sm.G[s];
+
+    // X = K S^T, Y = Q S^T (the split state dies here).
+    f32x4 X[4], Y[4];
+    {
+        Split8 sB[KB];
+#pragma unroll
+        for (int p = 0; p < KB; ++p) {
+            const float x[8] = {st[2 * p][0], st[2 * p][1], st[2 * p][2], st[2 * p][3],
+                                st[2 * p + 1][0], st[2 * p + 1][1], st[2 * p + 1][2], st[2 * p + 1][3]};
+            sB[p] = split8(x);
+        }
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            X[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            Y[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const int t = 16 * tt + lr;
+#pragma unroll
+            for (int p = 0; p < KB; ++p) {
+                const bf16x8 ka = kq_row8<DK>(Kc, t, p, lg);
+                const bf16x8 qa = kq_row8<DK>(Qc, t, p, lg);
+                X[tt] = mma(ka, sB[p].hi, X[tt]);
+                X[tt] = mma(ka, sB[p].lo, X[tt]);
+                Y[tt] = mma(qa, sB[p].hi, Y[tt]);
+                Y[tt] = mma(qa, sB[p].lo, Y[tt]);
+            }
+        }
+    }
+    // R = diag(beta) (V - diag(gamma) X) at rows t = 16 tt + 4 lg + r, split as
+    // the B operand of D = Linv R.  v[t][16 w + lr] by transposed reads.
+    Split8 rB[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        float x[8];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int tt = 2 * p + hh, t0 = 16 * tt + 4 * lg;
+            const bf16x4 vt = read_tr(sm.V[s] + (t0 + (lr >> 2)) * 64 + 32 * w + 8 * (lr & 3));
+            const float4 ga = *reinterpret_cast<const float4 *>(Gc + t0);
+            const float4 be = *reinterpret_cast<const float4 *>(Gc + 128 + t0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                x[4 * hh + r] = (&be.x)[r] * (static_cast<float>(vt[r]) - (&ga.x)[r] * X[tt][r]);
+        }
+        rB[p] = split8(x);
+    }
+    // D = Linv R (Linv is lower triangular: blocks p <= tt / 2).
+    f32x4 D[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+        D[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int t = 16 * tt + lr;
+#pragma unroll
+        for (int p = 0; p <= tt / 2; ++p) {
+            Split8 a;
+            a.hi = mat_row8(Mc, 0, t, p, lg);
+            a.lo = mat_row8(Mc, 1, t, p, lg);
+            D[tt] = mma3(a, rB[p], D[tt]);
+        }
+    }
+    // D split twice: as is (for P D) and scaled by e (for the state update).
+    Split8 dB[2], eB[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        float x[8], y[8];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int tt = 2 * p + hh;
+            const float4 ee = *reinterpret_cast<const float4 *>(Gc + 64 + 16 * tt + 4 * lg);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                x[4 * hh + r] = D[tt][r];
+                y[4 * hh + r] = (&ee.x)[r] * D[tt][r];
+            }
+        }
+        dB[p] = split8(x);
+        eB[p] = split8(y);
+    }
+    // O = diag(gamma) Y + P D, staged in LDS (this wave's 16 columns), then
+    // stored as 64-byte row segments.
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+        const int t = 16 * tt + lr;
+        const float4 ga = *reinterpret_cast<const float4 *>(Gc + 16 * tt + 4 * lg);
+        f32x4 Ot = Y[tt];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Ot[r] *= (&ga.x)[r];
+#pragma unroll
+        for (int p = 0; p <= tt / 2; ++p) {
+            Split8 a;
+            a.hi = mat_row8(Mc, 2, t, p, lg);
+            a.lo = mat_row8(Mc, 3, t, p, lg);
+            Ot = mma3(a, dB[p], Ot);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sm.O[16 * tt + 4 * lg + r][16 * w + lr] = Ot[r];
+    }
+    // The wave's own LDS writes complete before its later reads (in-order LDS
+    // per wave); the compiler barrier keeps the compiler from reordering them.
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int row = 16 * m + (lane >> 2), col = 16 * w + 4 * (lane & 3);
+        const float4 v4 = *reinterpret_cast<const float4 *>(&sm.O[row][col]);
+        if (row < n) *reinterpret_cast<float4 *>(obase + size_t(row) * ostride + col) = v4;
+    }
+    // S <- gamma_last S + K^T diag(e) D; K^T by transposed reads of the row-major
+    // keys: lane (lr, lg) takes keys 16 kt + lr at t = 32p + 4lg + {0..3} and
+    // 32p + 16 + 4lg + {0..3}.
+    const float glast = Gc[n - 1];
+    const int h8 = (lr & 1) << 3;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+        f32x4 U = {0.f, 0.f, 0.f, 0.f};
+        const int piece = 2 * kt + ((lr & 3) >> 1);
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const int ta = 32 * p + 4 * lg + (lr >> 2);
+            const bf16x8 ka = cat4(read_tr(Kc + kq_off<DK>(ta, piece) + h8),
+                                   read_tr(Kc + kq_off<DK>(ta + 16, piece) + h8));
+            U = mma(ka, eB[p].hi, U);
+            U = mma(ka, eB[p].lo, U);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st[kt][r] = glast * st[kt][r] + U[r];
+    }
+}
+
+template <int DK, int DV>
+__global__ __launch_bounds__(128) void prefill_scan_kernel(
     float *__restrict__ S, const __hip_bfloat16 *__restrict__ q, const __hip_bfloat16 *__restrict__ k,
     const __hip_bfloat16 *__restrict__ v, int L, int H, int nchunks, const float *__restrict__ ws,
     float *__restrict__ o) {
-    constexpr int RS = 16 * NWS;
+    constexpr int RS = 32;                 // value rows per workgroup (2 waves of 16)
     constexpr int SLICES = DV / RS;
     constexpr int KT = DK / 16;
-    constexpr int NT = 64 * NWS;
-    static_assert(SLICES * RS == DV, "tiling");
+    constexpr int NKQ = C * DK * 2 / 1024;  // 1 KiB blocks of a key or query chunk
+    static_assert(SLICES * RS == DV && NKQ % 2 == 0, "tiling");
 
-    __shared__ Smem<DK> sm;
+    __shared__ ScanLds<DK> sm;
 
     // Workgroup i runs on XCD i % 8.  The SLICES workgroups of one head read the
     // same keys, queries and chunk matrices, so they are placed on one XCD, where
@@ -655,7 +830,6 @@ __global__ __launch_bounds__(64 * NWS) void prefill_scan_kernel(
     const int lr = lane & 15, lg = lane >> 4;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int irow = slice * RS + w * 16 + lr;
-    const uint8_t *wsh = reinterpret_cast<const uint8_t *>(ws) + size_t(bh) * nchunks * kPrepBytes;
 
     float *Srow = S + (size_t(bh) * DV + irow) * DK;
     float st[KT][4];
@@ -668,34 +842,57 @@ __global__ __launch_bounds__(64 * NWS) void prefill_scan_kernel(
         st[kt][3] = s4.w;
     }
 
-    ChunkKQ<DK, NT> kq;
-    ChunkMats<DK, NT> mats;
-    ChunkV cv;
-    {
-        const int n0 = min(C, L);
-        kq.load(k, q, size_t(b) * L, n0, H, h, tid);
-        mats.load(wsh, tid);
-        cv.load(v, size_t(b) * L, n0, H, h, DV, irow, lg);
-    }
+    const __hip_bfloat16 *kb = k + (size_t(b) * L * H + h) * DK;   // token row t at + t H DK
+    const __hip_bfloat16 *qb = q + (size_t(b) * L * H + h) * DK;
+    const __hip_bfloat16 *vb = v + (size_t(b) * L * H + h) * DV + slice * RS;
+    const uint8_t *wsh = reinterpret_cast<const uint8_t *>(ws) + size_t(bh) * nchunks * kPrepBytes;
+    const size_t kstride = size_t(H) * DK, vstride = size_t(H) * DV;
+
+    // Copy chunk cn's operands into stage cn & 1.  Wave w takes the 1 KiB blocks
+    // w, w + 2, ...; rows past the prompt read the last token (finite data that
+    // beta = e = 0 cancels; their outputs are not stored).
+    auto issue = [&](int cn) {
+        const int s = cn & 1, c0 = cn * C;
+#pragma unroll
+        for (int u = 0; u < NKQ / 2; ++u) {
+            const int blk = 2 * u + w, byte = blk * 1024 + 16 * lane;
+            const int row = byte / (2 * DK), slot = (byte % (2 * DK)) >> 4;
+            const int piece = DK == 128 ? (slot ^ swz16(row)) : (slot ^ swz8(row));
+            const size_t off = size_t(min(c0 + row, L - 1)) * kstride + 8 * piece;
+            dma16(kb + off, __builtin_amdgcn_readfirstlane(lds_addr(sm.K[s]) + blk * 1024));
+            dma16(qb + off, __builtin_amdgcn_readfirstlane(lds_addr(sm.Q[s]) + blk * 1024));
+        }
+        const uint8_t *rec = wsh + size_t(cn) * kPrepBytes;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int blk = 2 * u + w, byte = blk * 1024 + 16 * lane;
+            const int arr = byte >> 13, row = (byte & 8191) >> 7, slot = (byte & 127) >> 4;
+            dma16(rec + (arr << 13) + (row << 7) + ((slot ^ swz8(row)) << 4),
+                  __builtin_amdgcn_readfirstlane(lds_addr(sm.M[s]) + blk * 1024));
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int blk = 2 * u + w, byte = blk * 1024 + 16 * lane;
+            const int row = byte >> 6, piece = (byte & 63) >> 4;
+            dma16(vb + size_t(min(c0 + row, L - 1)) * vstride + 8 * piece,
+                  __builtin_amdgcn_readfirstlane(lds_addr(sm.V[s]) + blk * 1024));
+        }
+        if (w == 0)
+            dma16(rec + kPrepMatBytes + 16 * min(lane, 3 * C / 4 - 1),
+                  __builtin_amdgcn_readfirstlane(lds_addr(sm.G[s])));
+    };
+
+    issue(0);
     for (int c = 0; c < nchunks; ++c) {
         const int c0 = c * C, n = min(C, L - c0);
-        const size_t row0 = size_t(b) * L + c0;
-        kq.store(sm, n, tid);
-        mats.store(sm, tid);
-        float vv[4][4];
-        cv.get(vv, n, lg);
-        __syncthreads();
-        // Prefetch the next chunk (the last chunk again at the end: valid
-        // addresses, no branch).
-        {
-            const int cn = min(c + 1, nchunks - 1), c0n = cn * C, nn = min(C, L - c0n);
-            const size_t row0n = size_t(b) * L + c0n;
-            kq.load(k, q, row0n, nn, H, h, tid);
-            mats.load(wsh + size_t(cn) * kPrepBytes, tid);
-            cv.load(v, row0n, nn, H, h, DV, irow, lg);
-        }
-        chunk_state<DK, false>(sm, st, vv, n, lane, o + (row0 * H + h) * DV + irow, size_t(H) * DV);
-        __syncthreads();  // the next chunk overwrites the shared buffers
+        // This chunk's copies (issued one chunk ago) have landed, for every wave,
+        // and every wave is done with the buffers the next copies overwrite.
+        __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) expcnt(7) lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (c + 1 < nchunks) issue(c + 1);
+        scan_chunk<DK>(sm, c & 1, st, n, lane, w, o + ((size_t(b) * L + c0) * H + h) * DV + slice * RS,
+                       size_t(H) * DV);
     }
 
 #pragma unroll
@@ -718,10 +915,8 @@ hipError_t launch_dk_dv(float *S, const void *q, const void *k, const void *v, c
                            qq, kk, g, beta, L, s.H, nchunks, static_cast<float *>(ws));
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        constexpr int NWS = 2;  // 32 value rows per workgroup: more compute units on the scan
-        hipLaunchKernelGGL((prefill_scan_kernel<DK, DV, NWS>), dim3(unsigned(heads * (DV / (16 * NWS)))),
-                           dim3(64 * NWS), 0, st, S, qq, kk, vv, L, s.H, nchunks,
-                           static_cast<const float *>(ws), o);
+        hipLaunchKernelGGL((prefill_scan_kernel<DK, DV>), dim3(unsigned(heads * (DV / 32))), dim3(128), 0, st,
+                           S, qq, kk, vv, L, s.H, nchunks, static_cast<const float *>(ws), o);
         return hipGetLastError();
     }
     // One pass: one workgroup per head.
