@@ -23,6 +23,9 @@ ARCH = os.environ.get("GDN_OFFLOAD_ARCH", "gfx950")
 HIPFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs rather than AGPRs: the kernels feed them straight to
+    # VALU work, and every AGPR result would cost a v_accvgpr_read.
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-command-line-argument",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]

@@ -600,20 +600,34 @@ __device__ inline void dma16(const void *src, uint32_t lds_base) {
                  : "memory", "m0");
 }
 
+// The same with a uniform 64-bit base in SGPRs and a 32-bit per-lane byte
+// offset (the saddr form): no per-lane 64-bit address arithmetic.
+__device__ inline void dma16s(const void *sbase, uint32_t voff, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_base), "v"(voff), "s"(sbase)
+                 : "memory", "m0");
+}
+
 __device__ inline uint32_t lds_addr(const void *p) {
     return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void *)p));
 }
 
+// Operand mapping of the scan.  The 16 rows of result tile tt (a 16x16 MFMA
+// tile over tokens) are the tokens tau(tt, m) = 32 (tt/2) + 8 (m/4) + 4 (tt%2) +
+// m%4, m = 0..15, and the contraction slots of block p for lane group lg are the
+// 8 consecutive indices 32p + 8lg .. + 7.  A D-layout lane (lr, lg) of tiles 2p
+// and 2p + 1 then holds exactly tokens 32p + 8lg .. + 7 (4 from each tile), the
+// slots of a B operand over tokens; and every A operand is one 16-byte LDS
+// read.  The state is kept the same way over keys: st[kt][r] is key
+// 32 (kt/2) + 8 lg + 4 (kt%2) + r of value row irow.
+__device__ inline int tau(int tt, int m) { return 32 * (tt >> 1) + 8 * (m >> 2) + 4 * (tt & 1) + (m & 3); }
+
 // LDS layouts.  Rows of keys/queries (256 B at dk = 128, 128 B at dk = 64) and
 // of the [C][C] matrices (128 B) keep their 16-byte pieces in an XOR-swizzled
-// order, slot = piece ^ swz(row), so that both the row reads of the MFMA A
-// operands (16 consecutive rows, one piece each) and the transposed reads of
-// the state update (4 consecutive rows, 4 half-pieces) hit distinct banks.
-__device__ inline int swz16(int t) { return ((t & 3) << 2) | ((t >> 2) & 3); }  // 16 pieces a row
-__device__ inline int swz8(int t) {                                               // 8 pieces a row
-    const int y = (t >> 1) & 7;
-    return ((y & 1) << 1) | ((y >> 1) & 1) | (y & 4);
-}
+// order, slot = piece ^ swz(row), chosen so that the A-operand row reads (16
+// rows 8 (m/4) + m%4 apart, one piece each) and the transposed reads of the
+// state update (4 consecutive rows x 4 pieces) hit distinct banks.
+__device__ inline int swz16(int t) { return ((t & 3) << 2) | ((t >> 3) & 3); }        // 16 pieces a row
+__device__ inline int swz8(int t) { return (((t >> 1) & 1) << 2) | ((t >> 3) & 3); }   // 8 pieces a row
 template <int DK>
 __device__ inline int kq_off(int t, int piece) {  // byte offset of a key/query piece
     if constexpr (DK == 128)
@@ -625,6 +639,8 @@ __device__ inline int mat_off(int arr, int t, int piece) {  // byte offset in th
     return arr * (C * C * 2) + t * 128 + ((piece ^ swz8(t)) << 4);
 }
 
+constexpr int kOStride = 36;  // floats per output staging row (16-byte aligned, fewer conflicts)
+
 template <int DK>
 struct alignas(16) ScanLds {
     uint8_t K[2][C * DK * 2];
@@ -632,41 +648,41 @@ struct alignas(16) ScanLds {
     uint8_t M[2][4 * C * C * 2];   // Linv hi, Linv lo, P hi, P lo
     uint8_t V[2][C * 32 * 2];      // the workgroup's 32 value columns, [t][32] bf16
     float G[2][256];               // gamma, e, beta (3 x 64), padded to 1 KiB
-    float O[C][32];                // output staging, wave w owns columns 16w .. 16w + 15
+    float O[C * kOStride];         // output staging, wave w owns columns 16w .. 16w + 15
 };
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 
 // ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
 // i % 4 of the 8 bytes addressed by lane 4 e + i / 4, for e = 0..3.  With lane
-// j addressing row r0 + j / 4, columns c0 + 4 (j % 4) .. + 3 of a row-major
-// 16-bit matrix, lane i receives rows r0 .. r0 + 3 of column c0 + i.
+// j addressing row r0 + j / 4 at column c(j % 4) .. + 3 of a row-major 16-bit
+// matrix, lane i receives rows r0 .. r0 + 3 of column c(i / 4) + i % 4.
 __device__ inline bf16x4 read_tr(const uint8_t *p) {
     const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)p);
     return __builtin_bit_cast(bf16x4, r);
 }
 
-// A operand of a 16-row tile from a swizzled row layout: row t, columns
-// (contraction slots) 32p + 4lg + {0..3} and 32p + 16 + 4lg + {0..3}.
+__device__ inline bf16x8 lds16(const uint8_t *p) { return *reinterpret_cast<const bf16x8 *>(p); }
+
+// Store the wave's 16 staged output columns of one chunk as 64-byte row
+// segments (rows < n).  obase points at o for the chunk's first token and the
+// workgroup's first value column; ostride is one token.
 template <int DK>
-__device__ inline bf16x8 kq_row8(const uint8_t *base, int t, int p, int lg) {
-    const int h8 = (lg & 1) << 3;
-    return cat4(*reinterpret_cast<const bf16x4 *>(base + kq_off<DK>(t, 4 * p + (lg >> 1)) + h8),
-                *reinterpret_cast<const bf16x4 *>(base + kq_off<DK>(t, 4 * p + 2 + (lg >> 1)) + h8));
-}
-__device__ inline bf16x8 mat_row8(const uint8_t *base, int arr, int t, int p, int lg) {
-    const int h8 = (lg & 1) << 3;
-    return cat4(*reinterpret_cast<const bf16x4 *>(base + mat_off(arr, t, 4 * p + (lg >> 1)) + h8),
-                *reinterpret_cast<const bf16x4 *>(base + mat_off(arr, t, 4 * p + 2 + (lg >> 1)) + h8));
+__device__ inline void scan_store_o(const ScanLds<DK> &sm, int n, int lane, int w, float *__restrict__ obase,
+                                    size_t ostride) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int row = 16 * m + (lane >> 2), col = 16 * w + 4 * (lane & 3);
+        const float4 v4 = *reinterpret_cast<const float4 *>(&sm.O[row * kOStride + col]);
+        if (row < n) *reinterpret_cast<float4 *>(obase + size_t(row) * ostride + col) = v4;
+    }
 }
 
 // State-coupled products of one chunk for one wave's 16 value rows, from stage
-// s of the LDS buffers (the same products as chunk_state).  obase points at o
-// for the chunk's first token and the workgroup's first value column; ostride
-// is one token.
+// s of the LDS buffers (the products of chunk_state, in the operand mapping
+// above).  The outputs are left in the staging buffer (this wave's columns).
 template <int DK>
-__device__ inline void scan_chunk(ScanLds<DK> &sm, int s, float (&st)[DK / 16][4], int n, int lane, int w,
-                                  float *__restrict__ obase, size_t ostride) {
+__device__ inline void scan_chunk(ScanLds<DK> &sm, int s, float (&st)[DK / 16][4], int n, int lane, int w) {
     constexpr int KT = DK / 16, KB = DK / 32;
     const int lr = lane & 15, lg = lane >> 4;
     const uint8_t *Kc = sm.K[s], *Qc = sm.Q[s], *Mc = sm.M[s];
@@ -686,11 +702,11 @@ __device__ inline void scan_chunk(ScanLds<DK> &sm, int s, float (&st)[DK / 16][4
         for (int tt = 0; tt < 4; ++tt) {
             X[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
             Y[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const int t = 16 * tt + lr;
+            const int t = tau(tt, lr);
 #pragma unroll
             for (int p = 0; p < KB; ++p) {
-                const bf16x8 ka = kq_row8<DK>(Kc, t, p, lg);
-                const bf16x8 qa = kq_row8<DK>(Qc, t, p, lg);
+                const bf16x8 ka = lds16(Kc + kq_off<DK>(t, 4 * p + lg));
+                const bf16x8 qa = lds16(Qc + kq_off<DK>(t, 4 * p + lg));
                 X[tt] = mma(ka, sB[p].hi, X[tt]);
                 X[tt] = mma(ka, sB[p].lo, X[tt]);
                 Y[tt] = mma(qa, sB[p].hi, Y[tt]);
@@ -698,15 +714,15 @@ __device__ inline void scan_chunk(ScanLds<DK> &sm, int s, float (&st)[DK / 16][4
             }
         }
     }
-    // R = diag(beta) (V - diag(gamma) X) at rows t = 16 tt + 4 lg + r, split as
-    // the B operand of D = Linv R.  v[t][16 w + lr] by transposed reads.
+    // R = diag(beta) (V - diag(gamma) X): lane (lr, lg) of tile tt = 2p + hh holds
+    // tokens t0 + r, t0 = 32p + 8lg + 4hh; v[t0 + r][16w + lr] by a transposed read.
     Split8 rB[2];
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
         float x[8];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-            const int tt = 2 * p + hh, t0 = 16 * tt + 4 * lg;
+            const int tt = 2 * p + hh, t0 = 32 * p + 8 * lg + 4 * hh;
             const bf16x4 vt = read_tr(sm.V[s] + (t0 + (lr >> 2)) * 64 + 32 * w + 8 * (lr & 3));
             const float4 ga = *reinterpret_cast<const float4 *>(Gc + t0);
             const float4 be = *reinterpret_cast<const float4 *>(Gc + 128 + t0);
@@ -721,12 +737,12 @@ __device__ inline void scan_chunk(ScanLds<DK> &sm, int s, float (&st)[DK / 16][4
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
         D[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int t = 16 * tt + lr;
+        const int t = tau(tt, lr);
 #pragma unroll
         for (int p = 0; p <= tt / 2; ++p) {
             Split8 a;
-            a.hi = mat_row8(Mc, 0, t, p, lg);
-            a.lo = mat_row8(Mc, 1, t, p, lg);
+            a.hi = lds16(Mc + mat_off(0, t, 4 * p + lg));
+            a.lo = lds16(Mc + mat_off(1, t, 4 * p + lg));
             D[tt] = mma3(a, rB[p], D[tt]);
         }
     }
@@ -738,7 +754,7 @@ __device__ inline void scan_chunk(ScanLds<DK> &sm, int s, float (&st)[DK / 16][4
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             const int tt = 2 * p + hh;
-            const float4 ee = *reinterpret_cast<const float4 *>(Gc + 64 + 16 * tt + 4 * lg);
+            const float4 ee = *reinterpret_cast<const float4 *>(Gc + 64 + 32 * p + 8 * lg + 4 * hh);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 x[4 * hh + r] = D[tt][r];
@@ -748,48 +764,38 @@ __device__ inline void scan_chunk(ScanLds<DK> &sm, int s, float (&st)[DK / 16][4
         dB[p] = split8(x);
         eB[p] = split8(y);
     }
-    // O = diag(gamma) Y + P D, staged in LDS (this wave's 16 columns), then
-    // stored as 64-byte row segments.
+    // O = diag(gamma) Y + P D, staged in LDS (this wave's 16 columns; the
+    // previous chunk's were stored from there before this chunk began).
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
-        const int t = 16 * tt + lr;
-        const float4 ga = *reinterpret_cast<const float4 *>(Gc + 16 * tt + 4 * lg);
+        const int t = tau(tt, lr), t0 = 32 * (tt >> 1) + 8 * lg + 4 * (tt & 1);
+        const float4 ga = *reinterpret_cast<const float4 *>(Gc + t0);
         f32x4 Ot = Y[tt];
 #pragma unroll
         for (int r = 0; r < 4; ++r) Ot[r] *= (&ga.x)[r];
 #pragma unroll
         for (int p = 0; p <= tt / 2; ++p) {
             Split8 a;
-            a.hi = mat_row8(Mc, 2, t, p, lg);
-            a.lo = mat_row8(Mc, 3, t, p, lg);
+            a.hi = lds16(Mc + mat_off(2, t, 4 * p + lg));
+            a.lo = lds16(Mc + mat_off(3, t, 4 * p + lg));
             Ot = mma3(a, dB[p], Ot);
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sm.O[16 * tt + 4 * lg + r][16 * w + lr] = Ot[r];
+        for (int r = 0; r < 4; ++r) sm.O[(t0 + r) * kOStride + 16 * w + lr] = Ot[r];
     }
-    // The wave's own LDS writes complete before its later reads (in-order LDS
-    // per wave); the compiler barrier keeps the compiler from reordering them.
-    asm volatile("" ::: "memory");
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const int row = 16 * m + (lane >> 2), col = 16 * w + 4 * (lane & 3);
-        const float4 v4 = *reinterpret_cast<const float4 *>(&sm.O[row][col]);
-        if (row < n) *reinterpret_cast<float4 *>(obase + size_t(row) * ostride + col) = v4;
-    }
-    // S <- gamma_last S + K^T diag(e) D; K^T by transposed reads of the row-major
-    // keys: lane (lr, lg) takes keys 16 kt + lr at t = 32p + 4lg + {0..3} and
-    // 32p + 16 + 4lg + {0..3}.
+    // S <- gamma_last S + K^T diag(e) D.  Tile kt's A operand is K^T at keys
+    // 32 (kt/2) + 8 (lr/4) + 4 (kt%2) + lr%4 (row lr) and tokens 32p + 8lg + {0..7}
+    // (slots), two transposed reads of 4 token rows each.
     const float glast = Gc[n - 1];
-    const int h8 = (lr & 1) << 3;
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
         f32x4 U = {0.f, 0.f, 0.f, 0.f};
-        const int piece = 2 * kt + ((lr & 3) >> 1);
+        const int piece = 4 * (kt >> 1) + (lr & 3), h8 = (kt & 1) << 3;
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-            const int ta = 32 * p + 4 * lg + (lr >> 2);
+            const int ta = 32 * p + 8 * lg + (lr >> 2);
             const bf16x8 ka = cat4(read_tr(Kc + kq_off<DK>(ta, piece) + h8),
-                                   read_tr(Kc + kq_off<DK>(ta + 16, piece) + h8));
+                                   read_tr(Kc + kq_off<DK>(ta + 4, piece) + h8));
             U = mma(ka, eB[p].hi, U);
             U = mma(ka, eB[p].lo, U);
         }
@@ -831,11 +837,12 @@ __global__ __launch_bounds__(128) void prefill_scan_kernel(
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int irow = slice * RS + w * 16 + lr;
 
+    // State in registers: st[kt][r] = S[irow][32 (kt/2) + 8 lg + 4 (kt%2) + r].
     float *Srow = S + (size_t(bh) * DV + irow) * DK;
     float st[KT][4];
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
-        const float4 s4 = *reinterpret_cast<const float4 *>(Srow + 16 * kt + 4 * lg);
+        const float4 s4 = *reinterpret_cast<const float4 *>(Srow + 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1));
         st[kt][0] = s4.x;
         st[kt][1] = s4.y;
         st[kt][2] = s4.z;
@@ -849,39 +856,81 @@ __global__ __launch_bounds__(128) void prefill_scan_kernel(
     const size_t kstride = size_t(H) * DK, vstride = size_t(H) * DV;
 
     // Copy chunk cn's operands into stage cn & 1.  Wave w takes the 1 KiB blocks
-    // w, w + 2, ...; rows past the prompt read the last token (finite data that
-    // beta = e = 0 cancels; their outputs are not stored).
+    // w, w + 2, ...  Full chunks use uniform bases and per-lane offsets computed
+    // once; a partial last chunk clamps each lane's row to the last token (finite
+    // data that beta = e = 0 cancels; those outputs are not stored).
+    constexpr int RPB = 1024 / (2 * DK);      // key rows per 1 KiB block
+    const uint32_t kstride_b = uint32_t(kstride) * 2, vstride_b = uint32_t(vstride) * 2;
+    auto kq_piece = [&](int u) {             // swizzled piece of this lane in K/Q block 2u + w
+        const int row = (2 * u + w) * RPB + lane / (64 / RPB), slot = lane % (64 / RPB);
+        return DK == 128 ? (slot ^ swz16(row)) : (slot ^ swz8(row));
+    };
+    // Per-lane offsets within a block (the block's own offset is uniform).  The
+    // swizzles depend on the row modulo 32, so the K/Q pattern repeats every 4
+    // blocks of a wave and the matrices' every 2.
+    uint32_t vo_kq[4], vo_m[2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        vo_kq[j] = uint32_t(lane / (64 / RPB)) * kstride_b + 16u * uint32_t(kq_piece(j));
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int mrow = ((2 * j + w) & 7) * 8 + (lane >> 3);  // row of block 2j + w in its matrix
+        vo_m[j] = uint32_t(lane >> 3) * 128u + 16u * uint32_t((lane & 7) ^ swz8(mrow));
+    }
+    const uint32_t vo_v = uint32_t(lane >> 2) * vstride_b + 16u * uint32_t(lane & 3);
+    const uint32_t vo_g = 16u * uint32_t(min(lane, 3 * C / 4 - 1));
     auto issue = [&](int cn) {
         const int s = cn & 1, c0 = cn * C;
-#pragma unroll
-        for (int u = 0; u < NKQ / 2; ++u) {
-            const int blk = 2 * u + w, byte = blk * 1024 + 16 * lane;
-            const int row = byte / (2 * DK), slot = (byte % (2 * DK)) >> 4;
-            const int piece = DK == 128 ? (slot ^ swz16(row)) : (slot ^ swz8(row));
-            const size_t off = size_t(min(c0 + row, L - 1)) * kstride + 8 * piece;
-            dma16(kb + off, __builtin_amdgcn_readfirstlane(lds_addr(sm.K[s]) + blk * 1024));
-            dma16(qb + off, __builtin_amdgcn_readfirstlane(lds_addr(sm.Q[s]) + blk * 1024));
-        }
         const uint8_t *rec = wsh + size_t(cn) * kPrepBytes;
+        const uint32_t lk = lds_addr(sm.K[s]), lq = lds_addr(sm.Q[s]), lm = lds_addr(sm.M[s]),
+                       lv = lds_addr(sm.V[s]);
+        if (c0 + C <= L) {
+            const uint8_t *kc = reinterpret_cast<const uint8_t *>(kb + size_t(c0) * kstride);
+            const uint8_t *qc = reinterpret_cast<const uint8_t *>(qb + size_t(c0) * kstride);
+            const uint8_t *vc = reinterpret_cast<const uint8_t *>(vb + size_t(c0) * vstride);
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            const int blk = 2 * u + w, byte = blk * 1024 + 16 * lane;
-            const int arr = byte >> 13, row = (byte & 8191) >> 7, slot = (byte & 127) >> 4;
-            dma16(rec + (arr << 13) + (row << 7) + ((slot ^ swz8(row)) << 4),
-                  __builtin_amdgcn_readfirstlane(lds_addr(sm.M[s]) + blk * 1024));
-        }
+            for (int u = 0; u < NKQ / 2; ++u) {
+                const int blk = 2 * u + w;
+                const size_t boff = size_t(blk * RPB) * kstride_b;
+                dma16s(kc + boff, vo_kq[u & 3], lk + blk * 1024);
+                dma16s(qc + boff, vo_kq[u & 3], lq + blk * 1024);
+            }
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int blk = 2 * u + w, byte = blk * 1024 + 16 * lane;
-            const int row = byte >> 6, piece = (byte & 63) >> 4;
-            dma16(vb + size_t(min(c0 + row, L - 1)) * vstride + 8 * piece,
-                  __builtin_amdgcn_readfirstlane(lds_addr(sm.V[s]) + blk * 1024));
+            for (int u = 0; u < 16; ++u) {
+                const int blk = 2 * u + w;
+                dma16s(rec + blk * 1024, vo_m[u & 1], lm + blk * 1024);
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int blk = 2 * u + w;
+                dma16s(vc + size_t(16 * blk) * vstride_b, vo_v, lv + blk * 1024);
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < NKQ / 2; ++u) {
+                const int blk = 2 * u + w, row = blk * RPB + lane / (64 / RPB);
+                const size_t off = size_t(min(c0 + row, L - 1)) * kstride + 8 * kq_piece(u);
+                dma16(kb + off, lk + blk * 1024);
+                dma16(qb + off, lq + blk * 1024);
+            }
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const int blk = 2 * u + w;
+                dma16s(rec + blk * 1024, vo_m[u & 1], lm + blk * 1024);
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int blk = 2 * u + w, row = 16 * blk + (lane >> 2);
+                dma16(vb + size_t(min(c0 + row, L - 1)) * vstride + 8 * (lane & 3), lv + blk * 1024);
+            }
         }
-        if (w == 0)
-            dma16(rec + kPrepMatBytes + 16 * min(lane, 3 * C / 4 - 1),
-                  __builtin_amdgcn_readfirstlane(lds_addr(sm.G[s])));
+        if (w == 0) dma16s(rec + kPrepMatBytes, vo_g, lds_addr(sm.G[s]));
     };
 
+    // Outputs of chunk c leave through the staging buffer at the top of chunk
+    // c + 1, so the wait at the top of each chunk finds the stores long done.
+    float *ob = o + (size_t(b) * L * H + h) * DV + slice * RS;
+    const size_t ostride = size_t(H) * DV;
     issue(0);
     for (int c = 0; c < nchunks; ++c) {
         const int c0 = c * C, n = min(C, L - c0);
@@ -890,14 +939,19 @@ __global__ __launch_bounds__(128) void prefill_scan_kernel(
         __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) expcnt(7) lgkmcnt(0)
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
+        if (c > 0) scan_store_o<DK>(sm, C, lane, w, ob + size_t(c0 - C) * ostride, ostride);
         if (c + 1 < nchunks) issue(c + 1);
-        scan_chunk<DK>(sm, c & 1, st, n, lane, w, o + ((size_t(b) * L + c0) * H + h) * DV + slice * RS,
-                       size_t(H) * DV);
+        // The staged outputs were read (in-order LDS per wave) before this chunk
+        // overwrites them; the compiler barrier keeps that order.
+        asm volatile("" ::: "memory");
+        scan_chunk<DK>(sm, c & 1, st, n, lane, w);
     }
+    asm volatile("" ::: "memory");
+    scan_store_o<DK>(sm, L - (nchunks - 1) * C, lane, w, ob + size_t(nchunks - 1) * C * ostride, ostride);
 
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt)
-        *reinterpret_cast<float4 *>(Srow + 16 * kt + 4 * lg) =
+        *reinterpret_cast<float4 *>(Srow + 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1)) =
             make_float4(st[kt][0], st[kt][1], st[kt][2], st[kt][3]);
 }
 
