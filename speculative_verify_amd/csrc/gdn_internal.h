@@ -105,6 +105,41 @@ template <> __device__ inline float load1<__hip_bfloat16>(const __hip_bfloat16 *
 }
 
 // ---------------------------------------------------------------------------
+// Asynchronous global -> LDS copies.
+// ---------------------------------------------------------------------------
+// global_load_lds_dwordx4: lane l's 16 bytes from `src` land at LDS byte
+// lds_base + 16 l (each lane gathers from its own address).  Issued through
+// inline asm so that the compiler, which cannot count these copies precisely,
+// does not wait for all of them before every LDS read; the kernels wait for
+// them explicitly (s_waitcnt vmcnt) before reading what they copied.
+__device__ inline void dma16(const void *src, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(src)
+                 : "memory", "m0");
+}
+
+// 4 bytes per lane (global_load_lds_dword): lane l's word lands at lds_base + 4 l.
+__device__ inline void dma4(const void *src, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_base), "v"(src)
+                 : "memory", "m0");
+}
+
+// The same with a uniform 64-bit base in SGPRs and a 32-bit per-lane byte
+// offset (the saddr form): no per-lane 64-bit address arithmetic.
+__device__ inline void dma16s(const void *sbase, uint32_t voff, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_base), "v"(voff), "s"(sbase)
+                 : "memory", "m0");
+}
+
+__device__ inline uint32_t lds_addr(const void *p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void *)p));
+}
+
+
+// s_waitcnt immediate (gfx9 encoding) that waits until at most n vector memory
+// operations are outstanding, leaving the other counters unconstrained.
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// ---------------------------------------------------------------------------
 // Launchers (one per kernel family); each returns a hipError_t.
 // ---------------------------------------------------------------------------
 hipError_t launch_verify(const float *S, const void *q, const void *k, const void *v,

@@ -590,27 +590,6 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
 // of a double buffer, so the walk waits on memory once per chunk at most.
 // ---------------------------------------------------------------------------
 
-// global_load_lds_dwordx4: lane l's 16 bytes from `src` land at LDS byte
-// lds_base + 16 l (each lane gathers from its own address).  Issued through
-// inline asm so that the compiler, which cannot count these copies precisely,
-// does not wait for all of them before every LDS read; the scan waits for them
-// itself (vmcnt) at the top of each chunk.
-__device__ inline void dma16(const void *src, uint32_t lds_base) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(src)
-                 : "memory", "m0");
-}
-
-// The same with a uniform 64-bit base in SGPRs and a 32-bit per-lane byte
-// offset (the saddr form): no per-lane 64-bit address arithmetic.
-__device__ inline void dma16s(const void *sbase, uint32_t voff, uint32_t lds_base) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_base), "v"(voff), "s"(sbase)
-                 : "memory", "m0");
-}
-
-__device__ inline uint32_t lds_addr(const void *p) {
-    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void *)p));
-}
-
 // Operand mapping of the scan.  The 16 rows of result tile tt (a 16x16 MFMA
 // tile over tokens) are the tokens tau(tt, m) = 32 (tt/2) + 8 (m/4) + 4 (tt%2) +
 // m%4, m = 0..15, and the contraction slots of block p for lane group lg are the

@@ -50,17 +50,33 @@ __device__ inline void split_bf16(const float4 &a, const float4 &b, bf16x8 &hi, 
     }
 }
 
+// bf16 X rows are 2 dk bytes, unpadded, with their 16-byte pieces in swizzled
+// order (slot = piece ^ xswz(x)), so that 16 consecutive rows read at one piece
+// hit distinct banks.
+template <int DK>
+__device__ inline int xswz(int x) {
+    return DK == 128 ? (x & 15) : ((x >> 1) & 7);
+}
+template <int DK>
+__device__ inline int xoff(int x, int piece) {  // byte offset of piece `piece` of row x
+    return x * (2 * DK) + ((piece ^ xswz<DK>(x)) << 4);
+}
+
 // A operand row x of the bf16 X for key block p: keys 16(2p) + 4lg + {0..3} in
 // slots 0..3 and 16(2p+1) + 4lg + {0..3} in slots 4..7 (the keys a lane holds in
 // its state registers for that block).
-__device__ inline bf16x8 xrow_bf16(const __bf16 *Xb, int stride, int x, int p, int lg) {
-    const bf16x4 lo4 = *reinterpret_cast<const bf16x4 *>(Xb + x * stride + 32 * p + 4 * lg);
-    const bf16x4 hi4 = *reinterpret_cast<const bf16x4 *>(Xb + x * stride + 32 * p + 16 + 4 * lg);
+template <int DK>
+__device__ inline bf16x8 xrow_bf16(const uint8_t *Xb, int x, int p, int lg) {
+    const int h8 = (lg & 1) << 3;
+    const bf16x4 lo4 = *reinterpret_cast<const bf16x4 *>(Xb + xoff<DK>(x, 4 * p + (lg >> 1)) + h8);
+    const bf16x4 hi4 = *reinterpret_cast<const bf16x4 *>(Xb + xoff<DK>(x, 4 * p + 2 + (lg >> 1)) + h8);
     return __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// X rows: 0..T-1 hold k_1..k_T, T..2T-1 hold q_1..q_T, the rest are zero.
-// MT = number of 16-row MFMA tiles of X (1 for T <= 8, 2 for T <= 16).
+// X rows: 0..TM-1 hold k_1..k_TM, TM..2TM-1 hold q_1..q_TM (TM = 8 MT); rows of
+// t >= T repeat row T (bf16: finite data nothing reads the results of) or are
+// zero (fp32).  MT = number of 16-row MFMA tiles of X (1 for T <= 8, 2 for
+// T <= 16).
 template <int DK, int DV, typename TIn, int MT>
 __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void verify_kernel(
     const float *__restrict__ S, const TIn *__restrict__ q, const TIn *__restrict__ k,
@@ -71,23 +87,28 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void ve
     constexpr int NT = 4;            // 16-row MFMA tiles per wave (64 rows)
     constexpr int KM = DK / 16;      // 16-key groups (4 keys per lane group)
     constexpr int XR = 16 * MT;      // rows of X
-    constexpr int XS = DK + 4;       // LDS row stride of X, floats
+    constexpr int XS = DK + 4;       // LDS row stride of the fp32 X, floats
     constexpr int TM = 8 * MT;       // largest T for this instantiation
     constexpr int KH = KM / NW;      // key groups per wave for the Gram matrix
-    constexpr int NCH = (2 * TM * DK / 8 + NTH - 1) / NTH;  // 8-element X pieces per thread
-    constexpr int NVP = (TM * DV / 8 + NTH - 1) / NTH;      // 8-element V pieces per thread
     constexpr bool kBf16 = sizeof(TIn) == 2;
+    // fp32 inputs: staging pieces per thread (8 elements each).
+    constexpr int NCH = (2 * TM * DK / 8 + NTH - 1) / NTH;
+    constexpr int NVP = (TM * DV / 8 + NTH - 1) / NTH;
+    // bf16 inputs: 1 KiB copy blocks of K (and of Q) and of V.
+    constexpr int NBK = TM * DK * 2 / 1024, NBV = TM * DV * 2 / 1024;
+    constexpr int NSTATE = NT * KM;  // state loads per thread
     static_assert(NW * 64 == DV && KH * NW == KM, "shape");
+    static_assert(!kBf16 || (NBK >= 1 && NBV >= 1 && NSTATE <= 63), "copy blocks");
 
-    // X as fp32 (fp32 inputs) or as the exact bf16 inputs (bf16 inputs).
-    constexpr int XSB = DK + 8;      // LDS row stride of the bf16 X, elements
     __shared__ __attribute__((aligned(16))) float X[kBf16 ? 4 : XR * XS];
-    __shared__ __attribute__((aligned(16))) __bf16 Xb[kBf16 ? XR * XSB : 8];
-    __shared__ __attribute__((aligned(16))) float Vs[TM][DV];   // the block's values
+    __shared__ __attribute__((aligned(16))) uint8_t Xb[kBf16 ? XR * 2 * DK : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t Vb[kBf16 ? TM * DV * 2 : 16];   // bf16 [TM][DV]
+    __shared__ __attribute__((aligned(16))) float Vs[kBf16 ? 4 : TM * DV];          // fp32 [TM][DV]
     __shared__ float P[XR][DV + 1];               // [K;Q] S^T: rows x, columns value row
     __shared__ float gpart[NW][XR][XR + 1];       // per-wave partial Gram matrices
     __shared__ float coefM[TM][TM + 1], coefN[TM][TM + 1];
     __shared__ float Gs[TM], gam[TM], bs[TM];
+    __shared__ __attribute__((aligned(16))) float graw[64], braw[64];  // g_t, beta_t (t clamped)
 
     const int bh = blockIdx.x;
     const int b = bh / H, h = bh - b * H;
@@ -99,25 +120,57 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void ve
     // Loads, in the order they are consumed; every address is valid (clamped) and
     // no loaded register is touched until it is used, so all of them are in
     // flight together.
-    // 1. The block's keys, queries and values, 8 elements per piece.
-    In8<TIn> xin[NCH], vin[NVP];
-#pragma unroll
-    for (int u = 0; u < NCH; ++u) {
-        const int c = min(tid + u * NTH, 2 * T * DK / 8 - 1);
-        const int e = c * 8, r = e / DK, col = e - r * DK;
-        const bool isk = r < T;
-        const int t = isk ? r : r - T;
-        xin[u].load((isk ? k : q) + (size_t(b * T + t) * H + h) * DK + col);
+    // 1. Gates, copied into LDS (lane t of wave 0 copies g_t and beta_t): a
+    //    register load would be sunk by the compiler to its use, behind a wait for
+    //    the state.
+    if (w == 0) {
+        const size_t gi = size_t(b * T + min(lane, T - 1)) * H + h;
+        dma4(g + gi, lds_addr(graw));
+        dma4(beta + gi, lds_addr(braw));
     }
+    // 2. The block's keys, queries and values.  bf16: copied straight into LDS
+    //    (1 KiB blocks, round robin over the waves); fp32: 8-element pieces into
+    //    registers, staged below.
+    In8<TIn> xin[kBf16 ? 1 : NCH], vin[kBf16 ? 1 : NVP];
+    if constexpr (kBf16) {
+        const uint32_t lx = lds_addr(Xb), lv = lds_addr(Vb);
+        // Block j of K (of Q) holds rows 1024 j / (2 dk) ..; wave w copies blocks
+        // w, w + NW, ...  Lane l's piece sits at LDS row r, slot s and comes from
+        // token row min(r, T - 1), piece s ^ xswz(row of X).
 #pragma unroll
-    for (int u = 0; u < NVP; ++u) {
-        const int c = min(tid + u * NTH, T * DV / 8 - 1);
-        const int e = c * 8, t = e / DV, col = e - t * DV;
-        vin[u].load(v + (size_t(b * T + t) * H + h) * DV + col);
+        for (int jj = 0; jj < (NBK + NW - 1) / NW; ++jj) {
+            const int j = jj * NW + w;
+            if (NBK % NW == 0 || j < NBK) {
+                const int byte = j * 1024 + 16 * lane, r = byte / (2 * DK), slot = (byte % (2 * DK)) >> 4;
+                const size_t row = (size_t(b * T + min(r, T - 1)) * H + h) * DK;
+                dma16(k + row + 8 * (slot ^ xswz<DK>(r)), lx + j * 1024);
+                dma16(q + row + 8 * (slot ^ xswz<DK>(TM + r)), lx + TM * 2 * DK + j * 1024);
+            }
+        }
+#pragma unroll
+        for (int jj = 0; jj < (NBV + NW - 1) / NW; ++jj) {
+            const int j = jj * NW + w;
+            if (NBV % NW == 0 || j < NBV) {
+                const int byte = j * 1024 + 16 * lane, t = byte / (2 * DV), piece = (byte % (2 * DV)) >> 4;
+                dma16(v + (size_t(b * T + min(t, T - 1)) * H + h) * DV + 8 * piece, lv + j * 1024);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < NCH; ++u) {
+            const int c = min(tid + u * NTH, 2 * T * DK / 8 - 1);
+            const int e = c * 8, r = e / DK, col = e - r * DK;
+            const bool isk = r < T;
+            const int t = isk ? r : r - T;
+            xin[u].load((isk ? k : q) + (size_t(b * T + t) * H + h) * DK + col);
+        }
+#pragma unroll
+        for (int u = 0; u < NVP; ++u) {
+            const int c = min(tid + u * NTH, T * DV / 8 - 1);
+            const int e = c * 8, t = e / DV, col = e - t * DV;
+            vin[u].load(v + (size_t(b * T + t) * H + h) * DV + col);
+        }
     }
-    // 2. Gates: lane t of wave 0 holds g_t and beta_t.
-    const float gv = g[size_t(b * T + min(lane, T - 1)) * H + h];
-    const float bv = beta[size_t(b * T + min(lane, T - 1)) * H + h];
     // Compiler-only barrier: keep the loads above ahead of the state loads, so
     // consuming them never waits for the state.
     asm volatile("" ::: "memory");
@@ -130,43 +183,45 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void ve
         for (int m = 0; m < KM; ++m)
             sreg[nt][m] = *reinterpret_cast<const float4 *>(Sw + size_t(16 * nt) * DK + 16 * m);
 
-    // Stage X and V (fp32) and the keys' record copy; zero the padding rows.  The
-    // piece index is clamped exactly as for the loads: a thread past the end
-    // rewrites the last piece with the same data.  Unconditional use keeps the
-    // compiler from sinking the loads below the state loads.
     TIn *kcopy = reinterpret_cast<TIn *>(rec + RL.kcopy);
+    // The LDS copies were issued before the NSTATE state loads; loads complete in
+    // order, so once at most NSTATE are outstanding the copies have landed.
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(NSTATE));
+    asm volatile("" ::: "memory");
+    if constexpr (!kBf16) {
+        // Stage X and V (fp32); the piece index is clamped exactly as for the
+        // loads: a thread past the end rewrites the last piece with the same data.
 #pragma unroll
-    for (int u = 0; u < NCH; ++u) {
-        const int c = min(tid + u * NTH, 2 * T * DK / 8 - 1);
-        const int e = c * 8, r = e / DK, col = e - r * DK;
-        if constexpr (kBf16) {
-            xin[u].store_raw(reinterpret_cast<TIn *>(Xb + r * XSB + col));
-        } else {
-            *reinterpret_cast<float4 *>(X + r * XS + col) =
+        for (int u = 0; u < NCH; ++u) {
+            const int c = min(tid + u * NTH, 2 * T * DK / 8 - 1);
+            const int e = c * 8, r = e / DK, col = e - r * DK;
+            const int x = r < T ? r : TM + (r - T);
+            *reinterpret_cast<float4 *>(X + x * XS + col) =
                 make_float4(xin[u].get(0), xin[u].get(1), xin[u].get(2), xin[u].get(3));
-            *reinterpret_cast<float4 *>(X + r * XS + col + 4) =
+            *reinterpret_cast<float4 *>(X + x * XS + col + 4) =
                 make_float4(xin[u].get(4), xin[u].get(5), xin[u].get(6), xin[u].get(7));
+            if (r < T) xin[u].store_raw(kcopy + (size_t(b * T + r) * H + h) * DK + col);
         }
-        if (r < T) xin[u].store_raw(kcopy + (size_t(b * T + r) * H + h) * DK + col);
-    }
 #pragma unroll
-    for (int u = 0; u < NVP; ++u) {
-        const int c = min(tid + u * NTH, T * DV / 8 - 1);
-        const int e = c * 8, t = e / DV, col = e - t * DV;
-        *reinterpret_cast<float4 *>(&Vs[t][col]) =
-            make_float4(vin[u].get(0), vin[u].get(1), vin[u].get(2), vin[u].get(3));
-        *reinterpret_cast<float4 *>(&Vs[t][col + 4]) =
-            make_float4(vin[u].get(4), vin[u].get(5), vin[u].get(6), vin[u].get(7));
+        for (int u = 0; u < NVP; ++u) {
+            const int c = min(tid + u * NTH, T * DV / 8 - 1);
+            const int e = c * 8, t = e / DV, col = e - t * DV;
+            *reinterpret_cast<float4 *>(Vs + t * DV + col) =
+                make_float4(vin[u].get(0), vin[u].get(1), vin[u].get(2), vin[u].get(3));
+            *reinterpret_cast<float4 *>(Vs + t * DV + col + 4) =
+                make_float4(vin[u].get(4), vin[u].get(5), vin[u].get(6), vin[u].get(7));
+        }
+        for (int idx = tid; idx < 2 * (TM - T) * DK; idx += NTH) {
+            const int rr = idx / DK, x = rr < TM - T ? T + rr : TM + T + (rr - (TM - T));
+            X[x * XS + idx % DK] = 0.f;
+        }
     }
-    for (int idx = tid; idx < (XR - 2 * T) * DK; idx += NTH) {
-        if constexpr (kBf16)
-            Xb[(2 * T + idx / DK) * XSB + idx % DK] = static_cast<__bf16>(0.f);
-        else
-            X[(2 * T + idx / DK) * XS + idx % DK] = 0.f;
-    }
+    __syncthreads();
     if (w == 0) {
         // Log-decay prefix sums over the block, in one fixed order (a wave scan);
-        // the commit reuses the stored values.
+        // the commit reuses the stored values.  Read by the coefficients after
+        // the barrier that follows the Gram matrix.
+        const float gv = graw[lane], bv = braw[lane];
         float Gp = lane < T ? gv : 0.f;
 #pragma unroll
         for (int off = 1; off < TM; off <<= 1) {
@@ -180,7 +235,14 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void ve
             reinterpret_cast<float *>(rec + RL.G)[size_t(b * T + lane) * H + h] = Gp;
         }
     }
-    __syncthreads();
+    if constexpr (kBf16) {
+        // The block's keys into the record, from the LDS copy (unswizzled).
+        for (int c = tid; c < T * DK / 8; c += NTH) {
+            const int r = c / (DK / 8), piece = c - r * (DK / 8);
+            *reinterpret_cast<uint4 *>(kcopy + (size_t(b * T + r) * H + h) * DK + 8 * piece) =
+                *reinterpret_cast<const uint4 *>(Xb + xoff<DK>(r, piece));
+        }
+    }
 
     // Gram matrix X X^T, each wave over its share of the keys, while the state is
     // still arriving: exact on bf16 MFMA for bf16 rows, fp32 MFMA otherwise.
@@ -198,7 +260,7 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void ve
                 const int p = w * (KH / 2) + pp;
                 bf16x8 a[MT];
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) a[mt] = xrow_bf16(Xb, XSB, 16 * mt + lr, p, lg);
+                for (int mt = 0; mt < MT; ++mt) a[mt] = xrow_bf16<DK>(Xb, 16 * mt + lr, p, lg);
 #pragma unroll
                 for (int m1 = 0; m1 < MT; ++m1)
 #pragma unroll
@@ -240,7 +302,7 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void ve
 #pragma unroll
             for (int ww = 0; ww < NW; ++ww) {
                 kk += gpart[ww][t][j];
-                qk += gpart[ww][T + t][j];
+                qk += gpart[ww][TM + t][j];
             }
             const float dec = expf(Gs[t] - Gs[j]);
             coefM[t][j] = j < t ? bs[t] * dec * kk : 0.f;
@@ -265,7 +327,7 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void ve
                 split_bf16(sreg[nt][2 * p], sreg[nt][2 * p + 1], shi, slo);
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
-                    const bf16x8 a = xrow_bf16(Xb, XSB, 16 * mt + lr, p, lg);
+                    const bf16x8 a = xrow_bf16<DK>(Xb, 16 * mt + lr, p, lg);
                     acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, shi, acc[mt], 0, 0, 0);
                     acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, slo, acc[mt], 0, 0, 0);
                 }
@@ -303,11 +365,16 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void ve
 #pragma unroll
         for (int t = 0; t < TM; ++t) {
             if (t < T) {
-                float dt = bs[t] * (Vs[t][i] - gam[t] * P[t][i]);
+                float vt;
+                if constexpr (kBf16)
+                    vt = bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(Vb)[t * DV + i]);
+                else
+                    vt = Vs[t * DV + i];
+                float dt = bs[t] * (vt - gam[t] * P[t][i]);
 #pragma unroll
                 for (int j = 0; j < t; ++j) dt -= coefM[t][j] * d[j];
                 d[t] = dt;
-                float ot = gam[t] * P[T + t][i];
+                float ot = gam[t] * P[TM + t][i];
 #pragma unroll
                 for (int j = 0; j <= t; ++j) ot += coefN[t][j] * d[j];
                 const size_t idx = (size_t(b * T + t) * H + h) * DV + i;
