@@ -78,6 +78,16 @@ def commit_bytes(B, H, dk, dv, n, es):
     return 2 * B * H * dv * dk * 4 + B * n * H * (dv * 4 + dk * es + 4) + ctrl
 
 
+def fused_bytes(B, H, dk, dv, T, n, es):
+    """Algorithmic HBM bytes of one gdn_commit_verify launch at accepted length n:
+    the verify's bytes plus the commit's, less the commit's state read (the state
+    is read once for both)."""
+    extra = commit_bytes(B, H, dk, dv, n, es)
+    if n > 0:
+        extra -= B * H * dv * dk * 4
+    return verify_bytes(B, H, dk, dv, T, es) + extra
+
+
 def prefill_bytes(B, H, dk, dv, L):
     return B * L * H * (2 * dk + dv) * 2 + B * L * H * 8 + B * L * H * dv * 4 + 2 * B * H * dv * dk * 4
 
@@ -119,9 +129,10 @@ def load_traffic(kernel):
 
 
 def accept_count(args):
-    """Passes whose accepted lengths are drawn: warmup, the headline region and
-    the kernel-timing region."""
-    return args.warmup + 2 * args.steps
+    """Passes whose accepted lengths are drawn: warmup, the fused headline and
+    kernel-timing regions, and the two regions of separate calls (each with LAG
+    passes verified ahead)."""
+    return args.warmup + 4 * args.steps + 2 * LAG
 
 
 class KernelEvents:
@@ -223,51 +234,46 @@ def main():
     dt = torch.bfloat16
     es = 2
 
-    # Buffer sets: state, block inputs, outputs, record.
+    # Buffer sets: state, block inputs, outputs, two records (alternating).  Four
+    # sets rotate, so no kernel finds its 96 MiB state still in the 256 MB
+    # Infinity Cache from the previous kernel.
     sets = []
     for r in range(RING):
         x = make_inputs(LAYERS, HEADS, DK, DV, T, dtype=dt, seed=args.seed + r, device=dev,
                         device_gen=True)
         o = torch.empty(LAYERS, T, HEADS, DV, dtype=torch.float32, device=dev)
-        rec = G.new_record(x.S0, T, dt)
-        sets.append((x, o, rec))
+        recs = [G.new_record(x.S0, T, dt) for _ in range(3)]
+        sets.append((x, o, recs))
     total = accept_count(args)
     n_host = make_accepts(total, T, seed=args.seed)
     n_dev = n_host.view(total, 1).expand(total, LAYERS).contiguous().to(dev)
     pos = torch.zeros(LAYERS, dtype=torch.int32, device=dev)
 
-    # Pass p is verified on buffer set p % RING and committed LAG steps later:
-    # step s verifies pass s + LAG and commits pass s with n_host[s].
-    def verify(p):
-        x, o, rec = sets[p % RING]
-        G.gdn_verify_block(x.S0, x.q, x.k, x.v, x.g, x.beta, o, rec)
-
-    def commit(p):
-        x, _, rec = sets[p % RING]
-        G.gdn_commit(x.S0, rec, n_dev[p], pos)
-
-    for p in range(LAG):
-        verify(p)
-
-    def step(s, kev=None, evs=None):
+    # Fused path (the headline): step s runs on set s % RING one
+    # gdn_commit_verify -- commit the block pending there at n_host[s], then verify
+    # the set's next block -- alternating the set's first two records.
+    def fused(s, kev=None, evs=None):
+        x, o, recs = sets[s % RING]
+        visit = s // RING
         if evs is not None:
             kev.record(evs[0])
-        verify(s + LAG)
+        G.gdn_commit_verify(x.S0, recs[visit % 2], n_dev[s], x.q, x.k, x.v, x.g, x.beta, o,
+                            recs[(visit + 1) % 2], pos=pos)
         if evs is not None:
             kev.record(evs[1])
-        commit(s)
-        if evs is not None:
-            kev.record(evs[2])
 
+    for r in range(RING):  # a pending block on every set
+        x, o, recs = sets[r]
+        G.gdn_verify_block(x.S0, x.q, x.k, x.v, x.g, x.beta, o, recs[0])
     for s in range(args.warmup):
-        step(s)
+        fused(s)
     torch.cuda.synchronize()
 
     # Headline region: exactly `steps` passes back to back, nothing between the
     # launches, wall clock around device synchronisations.
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i)
+        fused(args.warmup + i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     n_timed = [int(v) for v in n_host[args.warmup:args.warmup + args.steps]]
@@ -277,34 +283,82 @@ def main():
     # stream around each kernel (the events add a little time of their own, so
     # these per-launch averages are upper bounds on the kernels' durations).
     kev = KernelEvents(torch, torch.cuda.current_stream())
-    evs = [[kev.new() for _ in range(3)] for _ in range(args.steps)]
     s1 = args.warmup + args.steps
+    evs = [[kev.new() for _ in range(2)] for _ in range(args.steps)]
     for i in range(args.steps):
-        step(s1 + i, kev, evs[i])
+        fused(s1 + i, kev, evs[i])
     torch.cuda.synchronize()
-    t_ver = [kev.ms(evs[i][0], evs[i][1]) for i in range(args.steps)]
-    t_com = [kev.ms(evs[i][1], evs[i][2]) for i in range(args.steps)]
+    t_fus = [kev.ms(e[0], e[1]) for e in evs]
     kev.free([e for ev in evs for e in ev])
-    n_kt = [int(v) for v in n_host[s1:s1 + args.steps]]
+    n_fk = [int(v) for v in n_host[s1:s1 + args.steps]]
+
+    # Separate calls: the same passes as gdn_verify_block + gdn_commit.  Pass p is
+    # verified on set p % RING and committed LAG steps later (so that a commit
+    # never finds the state its verify just read in the cache); the set's third
+    # record carries the block.
+    s2 = s1 + args.steps
+
+    def verify(p):
+        x, o, recs = sets[p % RING]
+        G.gdn_verify_block(x.S0, x.q, x.k, x.v, x.g, x.beta, o, recs[2])
+
+    def commit(p):
+        x, _, recs = sets[p % RING]
+        G.gdn_commit(x.S0, recs[2], n_dev[p], pos)
+
+    def separate(s, evs=None):
+        if evs is not None:
+            kev.record(evs[0])
+        verify(s + LAG)
+        if evs is not None:
+            kev.record(evs[1])
+        commit(s)
+        if evs is not None:
+            kev.record(evs[2])
+
+    for p in range(s2, s2 + LAG):
+        verify(p)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        separate(s2 + i)
+    torch.cuda.synchronize()
+    wall_sep = time.perf_counter() - t0
+    tokens_sep = sum(int(v) for v in n_host[s2:s2 + args.steps])
+    s3 = s2 + args.steps
+    for p in range(s3, s3 + LAG):  # re-prime (the headline region above consumed them)
+        verify(p)
+    evs = [[kev.new() for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        separate(s3 + i, evs[i])
+    torch.cuda.synchronize()
+    t_ver = [kev.ms(e[0], e[1]) for e in evs]
+    t_com = [kev.ms(e[1], e[2]) for e in evs]
+    kev.free([e for ev in evs for e in ev])
+    n_kt = [int(v) for v in n_host[s3:s3 + args.steps]]
+
+    avg_fus_ms = sum(t_fus) / len(t_fus)
     avg_ver_ms = sum(t_ver) / len(t_ver)
     avg_com_ms = sum(t_com) / len(t_com)
     vb = verify_bytes(LAYERS, HEADS, DK, DV, T, es)
+    fb_avg = sum(fused_bytes(LAYERS, HEADS, DK, DV, T, n, es) for n in n_fk) / len(n_fk)
     cb_avg = sum(commit_bytes(LAYERS, HEADS, DK, DV, n, es) for n in n_kt) / len(n_kt)
+    fus_gbs = fb_avg / (avg_fus_ms * 1e-3) / 1e9
     ver_gbs = vb / (avg_ver_ms * 1e-3) / 1e9
     com_gbs = cb_avg / (avg_com_ms * 1e-3) / 1e9
-    pass_gbs = (vb + cb_avg) / ((avg_ver_ms + avg_com_ms) * 1e-3) / 1e9
+
+    def entry(gbs, ms, nbytes, traffic):
+        return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "avg_launch_us": round(ms * 1e3, 2),
+                "algorithmic_bytes_per_launch": round(nbytes), "traffic": traffic}
 
     kernels = {
-        "gdn_verify": {"bound": "hbm", "achieved": round(ver_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                       "frac": round(ver_gbs / HBM_PEAK_GBS, 4), "avg_launch_us": round(avg_ver_ms * 1e3, 2),
-                       "algorithmic_bytes_per_launch": vb, "traffic": load_traffic("verify_kernel")},
-        "gdn_commit": {"bound": "hbm", "achieved": round(com_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                       "frac": round(com_gbs / HBM_PEAK_GBS, 4), "avg_launch_us": round(avg_com_ms * 1e3, 2),
-                       "algorithmic_bytes_per_launch": round(cb_avg), "traffic": load_traffic("commit_kernel")},
+        "gdn_commit_verify": entry(fus_gbs, avg_fus_ms, fb_avg, load_traffic("commit_verify_kernel")),
+        "gdn_verify": entry(ver_gbs, avg_ver_ms, vb, load_traffic("verify_kernel")),
+        "gdn_commit": entry(com_gbs, avg_com_ms, cb_avg, load_traffic("commit_kernel")),
     }
-    dominant = "gdn_commit" if avg_com_ms >= avg_ver_ms else "gdn_verify"
-    roof = dict(kernels[dominant])
-    roof["kernel"] = dominant
+    roof = dict(kernels["gdn_commit_verify"])
+    roof["kernel"] = "gdn_commit_verify"
 
     result = {
         "metric": "GDN verify tokens/s (48 layers, T=8) + % HBM peak; prefill tok/s + % MFMA peak",
@@ -322,10 +376,15 @@ def main():
         "config": {"workload": "speculative verify pass: 48 GDN layers x 32 heads, dk=dv=128, T=8 "
                                "(7 draft + 1 anchor), bf16 q/k/v, fp32 state, verify + commit at "
                                "n~U{0..8}",
+                   "path": "gdn_commit_verify (commit of the pending block and verify of the next "
+                           "in one pass over the state)",
                    "layers": LAYERS, "heads": HEADS, "dk": DK, "dv": DV, "T": T,
                    "input_dtype": "bf16", "tokens_committed": tokens},
         "rows_per_s": round(T * args.steps / wall, 1),
-        "pass_hbm_frac": round(pass_gbs / HBM_PEAK_GBS, 4),
+        "pass_hbm_frac": round(fus_gbs / HBM_PEAK_GBS, 4),
+        "separate_calls": {"tokens_per_s": round(tokens_sep / wall_sep, 1),
+                           "ms_per_step": round(wall_sep / args.steps * 1e3, 4),
+                           "path": "gdn_verify_block + gdn_commit"},
         "kernel_timing": {"events": kev.kind, "region": f"{args.steps} passes after the headline region"},
         "sources_sha256_16": sources_hash(),
         "roofline": roof,
@@ -439,8 +498,8 @@ def summarize_profiles(args):
     fetch_factor = calib_kib / (sum(fetch[k]["kib"] for k in cal) / len(cal))
     write_factor = calib_kib / (sum(write[k]["kib"] for k in cal) / len(cal))
 
-    def kernel_rows(tag):
-        ids = sorted(k for k, e in fetch.items() if tag in e["name"] and k in write)
+    def kernel_rows(tag, also=""):
+        ids = sorted(k for k, e in fetch.items() if tag in e["name"] and also in e["name"] and k in write)
         return [(k, fetch[k]["kib"] * 1024 * fetch_factor, write[k]["kib"] * 1024 * write_factor) for k in ids]
 
     es = 2
@@ -456,7 +515,25 @@ def summarize_profiles(args):
                "calibration": {"copy_kib": calib_kib, "dispatches": len(cal),
                                "fetch_factor": round(fetch_factor, 4), "write_factor": round(write_factor, 4)},
                "kernels": {}}
-    ver = kernel_rows("verify_kernel")
+    total = accept_count(args)
+    n_host = [int(v) for v in make_accepts(total, T, seed=args.seed)]
+
+    def summarize(rows, alg):
+        fr = sum(r[1] for r in rows) / len(rows)
+        wr = sum(r[2] for r in rows) / len(rows)
+        ab = sum(alg) / len(alg)
+        return {"dispatches": len(rows), "read_bytes": round(fr), "write_bytes": round(wr),
+                "hbm_bytes_per_launch": round(fr + wr), "algorithmic_bytes_per_launch": round(ab),
+                "traffic_over_algorithmic": round((fr + wr) / ab, 3)}
+
+    # The fused kernel's dispatch i runs pass i (warmup, headline, kernel-timing
+    # regions); the separate commits run passes warmup + 2 steps + i.
+    fus = kernel_rows("verify_kernel", ", true>")
+    if fus:
+        fus = fus[:total]
+        summary["kernels"]["commit_verify_kernel"] = summarize(
+            fus, [fused_bytes(LAYERS, HEADS, DK, DV, T, n_host[i], es) for i in range(len(fus))])
+    ver = kernel_rows("verify_kernel", ", false>")
     if ver:
         vb = verify_bytes(LAYERS, HEADS, DK, DV, T, es)
         fr = sum(r[1] for r in ver) / len(ver)
@@ -467,17 +544,10 @@ def summarize_profiles(args):
             "traffic_over_algorithmic": round((fr + wr) / vb, 3)}
     com = kernel_rows("commit_kernel")
     if com:
-        total = accept_count(args)
-        n_host = [int(v) for v in make_accepts(total, T, seed=args.seed)]
-        alg = [commit_bytes(LAYERS, HEADS, DK, DV, n_host[i], es) for i in range(min(len(com), total))]
-        com = com[:len(alg)]
-        fr = sum(r[1] for r in com) / len(com)
-        wr = sum(r[2] for r in com) / len(com)
-        ab = sum(alg) / len(alg)
-        summary["kernels"]["commit_kernel"] = {
-            "dispatches": len(com), "read_bytes": round(fr), "write_bytes": round(wr),
-            "hbm_bytes_per_launch": round(fr + wr), "algorithmic_bytes_per_launch": round(ab),
-            "traffic_over_algorithmic": round((fr + wr) / ab, 3)}
+        s2 = args.warmup + 2 * args.steps
+        com = com[:total - s2]
+        summary["kernels"]["commit_kernel"] = summarize(
+            com, [commit_bytes(LAYERS, HEADS, DK, DV, n_host[s2 + i], es) for i in range(len(com))])
     # Prefill: every call launches either prefill_kernel or prep + scan; per call.
     pk = kernel_rows("prefill_kernel<")
     pp = kernel_rows("prefill_prep_kernel")

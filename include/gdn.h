@@ -142,6 +142,37 @@ int gdn_commit(float *S, void *record, const int32_t *n_accepted, int32_t *pos,
                const gdn_shape *shp, void *hip_stream);
 
 /*
+ * Commit, then verify, in one pass over the state: exactly gdn_commit(S,
+ * record_prev, n_accepted, pos) followed by gdn_verify_block(S, q, k, v, g,
+ * beta, T, in_dt, shp, o, record_next, record_next_bytes), with each (instance,
+ * head) reading its state from memory once instead of twice.
+ *
+ * Source: the decode loop of the lithos-metal README, DSpark paragraph (each
+ * pass commits the accepted prefix of the previous block, then verifies the next
+ * drafted block) and "How it works" (a fused layer mixer keeps its state slice
+ * on chip instead of making another round trip to memory); the devdoido audit,
+ * DSpark section (the rewind follows every acceptance decision, before the next
+ * block).
+ *
+ *   record_prev  the record of the block to commit (as for gdn_commit); its
+ *                error bits, flags and pos are handled exactly as gdn_commit does.
+ *   record_next  the record the new block is written to (as for
+ *                gdn_verify_block); a different buffer from record_prev (the
+ *                two records alternate between passes).
+ *   other arguments as for gdn_commit and gdn_verify_block.
+ *
+ * The new block is verified from the committed state, or from the unchanged
+ * state for instances whose commit failed (their error bits are set in
+ * record_prev, as gdn_commit would set them).  Returns GDN_OK or a negative
+ * gdn_status; GDN_EINVAL also when record_prev == record_next or the two
+ * overlap.
+ */
+int gdn_commit_verify(float *S, void *record_prev, const int32_t *n_accepted, int32_t *pos,
+                      const void *q, const void *k, const void *v, const float *g, const float *beta,
+                      int32_t T, gdn_in_dtype in_dt, const gdn_shape *shp, float *o, void *record_next,
+                      size_t record_next_bytes, void *hip_stream);
+
+/*
  * Diagnostic: copy each instance's commit error bits (GDN_REC_*) into
  * host_err_bits[0..B-1].  Synchronises `hip_stream`.  Bits are cleared by the
  * next gdn_verify_block.

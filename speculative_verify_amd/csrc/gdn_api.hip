@@ -59,6 +59,29 @@ int gdn_commit(float *S, void *record, const int32_t *n_accepted, int32_t *pos,
                                     static_cast<hipStream_t>(hip_stream)));
 }
 
+int gdn_commit_verify(float *S, void *record_prev, const int32_t *n_accepted, int32_t *pos, const void *q,
+                      const void *k, const void *v, const float *g, const float *beta, int32_t T,
+                      gdn_in_dtype in_dt, const gdn_shape *shp, float *o, void *record_next,
+                      size_t record_next_bytes, void *hip_stream) {
+    int rc = check_shape(shp);
+    if (rc != GDN_OK) return rc;
+    if (!valid_dtype(in_dt)) return GDN_EINVAL;
+    if (!aligned(S, 16) || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+        !aligned(record_prev, 16) || !aligned(record_next, 16) || !aligned(g, 4) || !aligned(beta, 4) ||
+        !aligned(n_accepted, 4))
+        return GDN_EINVAL;
+    if (pos != nullptr && !aligned(pos, 4)) return GDN_EINVAL;
+    // The records must be distinct: record_prev may not start inside record_next
+    // (its own length is only known on the device).
+    const uintptr_t rp = reinterpret_cast<uintptr_t>(record_prev), rn = reinterpret_cast<uintptr_t>(record_next);
+    if (rp >= rn && rp < rn + record_next_bytes) return GDN_EINVAL;
+    if (rn > rp && rn - rp < 256) return GDN_EINVAL;  // overlaps record_prev's header at least
+    if (T < 1 || T > GDN_T_MAX) return GDN_ERANGE;
+    if (record_next_bytes < gdn_block_record_bytes(shp, T, in_dt)) return GDN_EWS;
+    return hip_status(launch_commit_verify(S, record_prev, n_accepted, pos, q, k, v, g, beta, T, in_dt, *shp, o,
+                                           record_next, static_cast<hipStream_t>(hip_stream)));
+}
+
 int gdn_record_status(const void *record, const gdn_shape *shp, int32_t *host_err_bits,
                       void *hip_stream) {
     int rc = check_shape(shp);

@@ -149,6 +149,11 @@ hipError_t launch_verify(const float *S, const void *q, const void *k, const voi
 hipError_t launch_commit(float *S, void *record, const int32_t *n_accepted, int32_t *pos,
                          const gdn_shape &shp, hipStream_t stream);
 
+hipError_t launch_commit_verify(float *S, void *record_prev, const int32_t *n_accepted, int32_t *pos,
+                                const void *q, const void *k, const void *v, const float *g,
+                                const float *beta, int T, gdn_in_dtype dt, const gdn_shape &shp, float *o,
+                                void *record_next, hipStream_t stream);
+
 hipError_t launch_prefill(float *S, const void *q, const void *k, const void *v,
                           const float *g, const float *beta, int L, gdn_in_dtype dt,
                           const gdn_shape &shp, float *o, void *ws, size_t ws_bytes,

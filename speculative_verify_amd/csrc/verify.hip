@@ -77,11 +77,17 @@ __device__ inline bf16x8 xrow_bf16(const uint8_t *Xb, int x, int p, int lg) {
 // t >= T repeat row T (bf16: finite data nothing reads the results of) or are
 // zero (fp32).  MT = number of 16-row MFMA tiles of X (1 for T <= 8, 2 for
 // T <= 16).
-template <int DK, int DV, typename TIn, int MT>
+//
+// FUSED: first commit the block pending in record `rprev` at n_acc[b] rows, as
+// the commit kernel does (same checks, error bits, flags and pos), applying the
+// rank-n update to each state tile as it arrives and writing S_n back; then
+// verify the new block from S_n.  Each (instance, head) reads its state once.
+template <int DK, int DV, typename TIn, int MT, bool FUSED>
 __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void verify_kernel(
-    const float *__restrict__ S, const TIn *__restrict__ q, const TIn *__restrict__ k,
+    float *__restrict__ S, const TIn *__restrict__ q, const TIn *__restrict__ k,
     const TIn *__restrict__ v, const float *__restrict__ g, const float *__restrict__ beta,
-    int T, int B, int H, float *__restrict__ o, uint8_t *__restrict__ rec) {
+    int T, int B, int H, float *__restrict__ o, uint8_t *__restrict__ rec, uint8_t *__restrict__ rprev,
+    const int32_t *__restrict__ n_acc, int32_t *__restrict__ pos) {
     constexpr int NW = DV / 64;      // waves per workgroup
     constexpr int NTH = 64 * NW;     // threads
     constexpr int NT = 4;            // 16-row MFMA tiles per wave (64 rows)
@@ -109,6 +115,12 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void ve
     __shared__ float coefM[TM][TM + 1], coefN[TM][TM + 1];
     __shared__ float Gs[TM], gam[TM], bs[TM];
     __shared__ __attribute__((aligned(16))) float graw[64], braw[64];  // g_t, beta_t (t clamped)
+    // FUSED: the first (up to) 8 replayed rows of the pending block: delta (then
+    // exp(G_n - G_j) delta), its keys (in the pending record's dtype) and G.
+    constexpr int CR = 8;
+    __shared__ __attribute__((aligned(16))) float cdraw[FUSED ? CR * DV : 4];
+    __shared__ __attribute__((aligned(16))) uint8_t kraw[FUSED ? CR * DK * 4 : 16];
+    __shared__ __attribute__((aligned(16))) float gprev[FUSED ? 64 : 4];
 
     const int bh = blockIdx.x;
     const int b = bh / H, h = bh - b * H;
@@ -116,6 +128,67 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void ve
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 15, lg = lane >> 4;
     const RecLayout RL = rec_layout(B, T, H, DK, DV, int(sizeof(TIn)));
+
+    // FUSED: the pending block's status (uniform over the workgroup).  cn rows
+    // are committed when ok; cerr is the instance's error bit otherwise.
+    int cn = 0, Tp = 1, esp = 2;
+    bool cok = false;
+    uint32_t cerr = 0;
+    RecLayout RLp{};
+    if constexpr (FUSED) {
+        const RecHeader *hp = reinterpret_cast<const RecHeader *>(rprev);
+        if (hp->magic != kRecMagic) {
+            cerr = GDN_REC_NO_BLOCK;
+        } else {
+            Tp = hp->T;
+            const int ipd = hp->in_dt;
+            if (hp->B != B || hp->H != H || hp->dk != DK || hp->dv != DV || Tp < 1 || Tp > GDN_T_MAX ||
+                (ipd != GDN_IN_F32 && ipd != GDN_IN_BF16)) {
+                cerr = b < hp->B ? uint32_t(GDN_REC_SHAPE) : 0u;
+            } else {
+                esp = ipd == GDN_IN_BF16 ? 2 : 4;
+                RLp = rec_layout(B, Tp, H, DK, DV, esp);
+                const uint32_t *fl = reinterpret_cast<const uint32_t *>(rprev + RLp.flags) + size_t(bh) * kCommitSlices;
+                bool valid = true;
+#pragma unroll
+                for (int sl = 0; sl < DV / kCommitRows; ++sl) valid = valid && fl[sl] == kRecValid;
+                const int n = n_acc[b];
+                if (!valid) {
+                    cerr = GDN_REC_NO_BLOCK;
+                } else if (n < 0 || n > Tp) {
+                    cerr = GDN_REC_N_RANGE;
+                } else {
+                    cok = true;
+                    cn = n;
+                }
+            }
+        }
+        cn = __builtin_amdgcn_readfirstlane(cn);
+        if (cn > 0) {
+            // Copy rows j < min(cn, CR) of delta (DV floats each) and of the keys
+            // (DK elements each), clamped to row cn - 1, and G_1..G_Tp.
+            const int nr = min(cn, CR);
+            const uint8_t *dsrc = rprev + RLp.delta;
+            const uint8_t *ksrc = rprev + RLp.kcopy;
+            const uint32_t lcd = lds_addr(cdraw), lk = lds_addr(kraw);
+            constexpr int DBLK = CR * DV * 4 / 1024;
+#pragma unroll
+            for (int jj = 0; jj < (DBLK + NW - 1) / NW; ++jj) {
+                const int blk = jj * NW + w;
+                if (DBLK % NW == 0 || blk < DBLK) {
+                    const int byte = blk * 1024 + 16 * lane, j = byte / (4 * DV), pc = byte % (4 * DV);
+                    dma16(dsrc + ((size_t(b) * Tp + min(j, nr - 1)) * H + h) * DV * 4 + pc, lcd + blk * 1024);
+                }
+            }
+            const int krow = DK * esp, kblk = CR * krow / 1024;  // 2 or 4 blocks (dk = 128)
+            for (int blk = w; blk < kblk; blk += NW) {
+                const int byte = blk * 1024 + 16 * lane, j = byte / krow, pc = byte % krow;
+                dma16(ksrc + ((size_t(b) * Tp + min(j, nr - 1)) * H + h) * krow + pc, lk + blk * 1024);
+            }
+            if (w == 0)
+                dma4(rprev + RLp.G + ((size_t(b) * Tp + min(lane, Tp - 1)) * H + h) * 4, lds_addr(gprev));
+        }
+    }
 
     // Loads, in the order they are consumed; every address is valid (clamped) and
     // no loaded register is touched until it is used, so all of them are in
@@ -175,18 +248,25 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void ve
     // consuming them never waits for the state.
     asm volatile("" ::: "memory");
     // 3. The wave's state rows 64w + 16nt + lr, keys 16m + 4lg .. +3, tile by tile.
+    //    The plain verify issues all four tiles at once; the fused kernel keeps two
+    //    tiles in flight and issues the next after writing one back, so that its
+    //    reads and write-backs share the memory system instead of queueing as a
+    //    read phase followed by a write phase.
+    constexpr int NPRE = FUSED ? 2 : NT;   // tiles loaded up front
     const float *Sw = S + (size_t(bh) * DV + 64 * w + lr) * DK + 4 * lg;
     float4 sreg[NT][KM];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+    auto load_tile = [&](int nt) {
 #pragma unroll
         for (int m = 0; m < KM; ++m)
             sreg[nt][m] = *reinterpret_cast<const float4 *>(Sw + size_t(16 * nt) * DK + 16 * m);
+    };
+#pragma unroll
+    for (int nt = 0; nt < NPRE; ++nt) load_tile(nt);
 
     TIn *kcopy = reinterpret_cast<TIn *>(rec + RL.kcopy);
-    // The LDS copies were issued before the NSTATE state loads; loads complete in
-    // order, so once at most NSTATE are outstanding the copies have landed.
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(NSTATE));
+    // The LDS copies were issued before the NPRE KM state loads; loads complete in
+    // order, so once at most that many are outstanding the copies have landed.
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(NPRE * KM));
     asm volatile("" ::: "memory");
     if constexpr (!kBf16) {
         // Stage X and V (fp32); the piece index is clamped exactly as for the
@@ -217,6 +297,18 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void ve
         }
     }
     __syncthreads();
+    float gam_n = 1.f;
+    if constexpr (FUSED) {
+        if (cn > 0) {
+            // exp(G_n - G_j) delta_j for this thread's value row (rows 64w .. 64w + 63
+            // belong to wave w, which is the only reader of them).
+            const float Gn = gprev[cn - 1];
+            gam_n = expf(Gn);
+#pragma unroll
+            for (int j = 0; j < CR; ++j)
+                if (j < cn) cdraw[j * DV + tid] *= expf(Gn - gprev[j]);
+        }
+    }
     if (w == 0) {
         // Log-decay prefix sums over the block, in one fixed order (a wave scan);
         // the commit reuses the stored values.  Read by the coefficients after
@@ -317,6 +409,76 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void ve
     // same keys in A and B.
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
+        if constexpr (FUSED) {
+            if (cn > 0) {
+                // S_n = exp(G_n) S + sum_{j < n} exp(G_n - G_j) delta_j k_j^T for this
+                // tile (row 64w + 16nt + lr, keys 16m + 4lg + {0..3}), written back.
+                const int row = 64 * w + 16 * nt + lr;
+#pragma unroll
+                for (int m = 0; m < KM; ++m) {
+                    sreg[nt][m].x *= gam_n;
+                    sreg[nt][m].y *= gam_n;
+                    sreg[nt][m].z *= gam_n;
+                    sreg[nt][m].w *= gam_n;
+                }
+                auto add_row = [&](float c, const float4 (&kv)[KM]) {
+#pragma unroll
+                    for (int m = 0; m < KM; ++m) {
+                        sreg[nt][m].x += c * kv[m].x;
+                        sreg[nt][m].y += c * kv[m].y;
+                        sreg[nt][m].z += c * kv[m].z;
+                        sreg[nt][m].w += c * kv[m].w;
+                    }
+                };
+                const int nr = min(cn, CR);
+                if (esp == 2) {
+#pragma unroll 1
+                    for (int j = 0; j < nr; ++j) {
+                        float4 kv[KM];
+#pragma unroll
+                        for (int m = 0; m < KM; ++m) {
+                            const uint2 r2 = *reinterpret_cast<const uint2 *>(kraw + (j * DK + 16 * m + 4 * lg) * 2);
+                            kv[m] = make_float4(__uint_as_float(r2.x << 16), __uint_as_float(r2.x & 0xffff0000u),
+                                                __uint_as_float(r2.y << 16), __uint_as_float(r2.y & 0xffff0000u));
+                        }
+                        add_row(cdraw[j * DV + row], kv);
+                    }
+                } else {
+#pragma unroll 1
+                    for (int j = 0; j < nr; ++j) {
+                        float4 kv[KM];
+#pragma unroll
+                        for (int m = 0; m < KM; ++m)
+                            kv[m] = *reinterpret_cast<const float4 *>(kraw + (j * DK + 16 * m + 4 * lg) * 4);
+                        add_row(cdraw[j * DV + row], kv);
+                    }
+                }
+                // Rows past CR (blocks longer than 8): straight from the record.
+#pragma unroll 1
+                for (int j = CR; j < cn; ++j) {
+                    const size_t rj = (size_t(b) * Tp + j) * H + h;
+                    const float c = expf(gprev[cn - 1] - reinterpret_cast<const float *>(rprev + RLp.G)[rj]) *
+                                    reinterpret_cast<const float *>(rprev + RLp.delta)[rj * DV + row];
+                    float4 kv[KM];
+#pragma unroll
+                    for (int m = 0; m < KM; ++m) {
+                        const int key = 16 * m + 4 * lg;
+                        if (esp == 2) {
+                            const uint2 r2 = *reinterpret_cast<const uint2 *>(rprev + RLp.kcopy + (rj * DK + key) * 2);
+                            kv[m] = make_float4(__uint_as_float(r2.x << 16), __uint_as_float(r2.x & 0xffff0000u),
+                                                __uint_as_float(r2.y << 16), __uint_as_float(r2.y & 0xffff0000u));
+                        } else {
+                            kv[m] = *reinterpret_cast<const float4 *>(rprev + RLp.kcopy + (rj * DK + key) * 4);
+                        }
+                    }
+                    add_row(c, kv);
+                }
+                float *Sw_out = S + (size_t(bh) * DV + row) * DK + 4 * lg;
+#pragma unroll
+                for (int m = 0; m < KM; ++m) *reinterpret_cast<float4 *>(Sw_out + 16 * m) = sreg[nt][m];
+            }
+            if (nt + NPRE < NT) load_tile(nt + NPRE);
+        }
         f32x4 acc[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -384,6 +546,17 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void ve
         }
     }
 
+    if constexpr (FUSED) {
+        // Retire the committed block (every thread read the flags above, before
+        // the barriers since) or report why nothing was committed.
+        if (cok && tid < DV / kCommitRows)
+            reinterpret_cast<uint32_t *>(rprev + RLp.flags)[size_t(bh) * kCommitSlices + tid] = 0u;
+        if (tid == 0 && h == 0) {
+            if (cok && pos) pos[b] += cn;
+            if (cerr) atomicOr(&reinterpret_cast<RecCtrl *>(rprev + 256)[b].err, cerr);
+        }
+    }
+
     // Mark the block pending for every commit workgroup of this head, clear the
     // instance's error bits; the header describes the record.
     if (tid < DV / kCommitRows)
@@ -401,32 +574,42 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void ve
     }
 }
 
-template <int DK, int DV, typename TIn>
-hipError_t launch_t(const float *S, const void *q, const void *k, const void *v, const float *g,
-                    const float *beta, int T, const gdn_shape &s, float *o, void *rec,
-                    hipStream_t st) {
+template <int DK, int DV, typename TIn, bool FUSED>
+hipError_t launch_t(float *S, const void *q, const void *k, const void *v, const float *g,
+                    const float *beta, int T, const gdn_shape &s, float *o, void *rec, void *rprev,
+                    const int32_t *n_acc, int32_t *pos, hipStream_t st) {
     const dim3 grid(unsigned(s.B) * unsigned(s.H)), block(DV);
     auto *qq = static_cast<const TIn *>(q);
     auto *kk = static_cast<const TIn *>(k);
     auto *vv = static_cast<const TIn *>(v);
     auto *rr = static_cast<uint8_t *>(rec);
+    auto *rp = static_cast<uint8_t *>(rprev);
     if (T <= 8)
-        hipLaunchKernelGGL((verify_kernel<DK, DV, TIn, 1>), grid, block, 0, st, S, qq, kk, vv, g,
-                           beta, T, s.B, s.H, o, rr);
+        hipLaunchKernelGGL((verify_kernel<DK, DV, TIn, 1, FUSED>), grid, block, 0, st, S, qq, kk, vv, g,
+                           beta, T, s.B, s.H, o, rr, rp, n_acc, pos);
     else
-        hipLaunchKernelGGL((verify_kernel<DK, DV, TIn, 2>), grid, block, 0, st, S, qq, kk, vv, g,
-                           beta, T, s.B, s.H, o, rr);
+        hipLaunchKernelGGL((verify_kernel<DK, DV, TIn, 2, FUSED>), grid, block, 0, st, S, qq, kk, vv, g,
+                           beta, T, s.B, s.H, o, rr, rp, n_acc, pos);
     return hipGetLastError();
 }
 
-template <typename TIn>
-hipError_t launch_dt(const float *S, const void *q, const void *k, const void *v, const float *g,
-                     const float *beta, int T, const gdn_shape &s, float *o, void *rec,
-                     hipStream_t st) {
-    if (s.dk == 128 && s.dv == 128) return launch_t<128, 128, TIn>(S, q, k, v, g, beta, T, s, o, rec, st);
-    if (s.dk == 128 && s.dv == 64) return launch_t<128, 64, TIn>(S, q, k, v, g, beta, T, s, o, rec, st);
-    if (s.dk == 64 && s.dv == 128) return launch_t<64, 128, TIn>(S, q, k, v, g, beta, T, s, o, rec, st);
-    return launch_t<64, 64, TIn>(S, q, k, v, g, beta, T, s, o, rec, st);
+template <bool FUSED>
+hipError_t launch_any(float *S, const void *q, const void *k, const void *v, const float *g, const float *beta,
+                      int T, gdn_in_dtype dt, const gdn_shape &s, float *o, void *rec, void *rprev,
+                      const int32_t *n_acc, int32_t *pos, hipStream_t st) {
+#define GDN_VERIFY_LAUNCH(DK_, DV_)                                                                        \
+    if (s.dk == DK_ && s.dv == DV_)                                                                       \
+        return dt == GDN_IN_BF16                                                                          \
+                   ? launch_t<DK_, DV_, __hip_bfloat16, FUSED>(S, q, k, v, g, beta, T, s, o, rec, rprev,  \
+                                                               n_acc, pos, st)                            \
+                   : launch_t<DK_, DV_, float, FUSED>(S, q, k, v, g, beta, T, s, o, rec, rprev, n_acc,    \
+                                                      pos, st);
+    GDN_VERIFY_LAUNCH(128, 128)
+    GDN_VERIFY_LAUNCH(128, 64)
+    GDN_VERIFY_LAUNCH(64, 128)
+    GDN_VERIFY_LAUNCH(64, 64)
+#undef GDN_VERIFY_LAUNCH
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -434,9 +617,17 @@ hipError_t launch_dt(const float *S, const void *q, const void *k, const void *v
 hipError_t launch_verify(const float *S, const void *q, const void *k, const void *v,
                          const float *g, const float *beta, int T, gdn_in_dtype dt,
                          const gdn_shape &shp, float *o, void *record, hipStream_t stream) {
-    if (dt == GDN_IN_BF16)
-        return launch_dt<__hip_bfloat16>(S, q, k, v, g, beta, T, shp, o, record, stream);
-    return launch_dt<float>(S, q, k, v, g, beta, T, shp, o, record, stream);
+    // The plain verify never writes S.
+    return launch_any<false>(const_cast<float *>(S), q, k, v, g, beta, T, dt, shp, o, record, nullptr, nullptr,
+                             nullptr, stream);
+}
+
+hipError_t launch_commit_verify(float *S, void *record_prev, const int32_t *n_accepted, int32_t *pos,
+                                const void *q, const void *k, const void *v, const float *g,
+                                const float *beta, int T, gdn_in_dtype dt, const gdn_shape &shp, float *o,
+                                void *record_next, hipStream_t stream) {
+    return launch_any<true>(S, q, k, v, g, beta, T, dt, shp, o, record_next, record_prev, n_accepted, pos,
+                            stream);
 }
 
 }  // namespace gdn

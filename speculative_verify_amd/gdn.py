@@ -28,6 +28,7 @@ EXPORTED = (
     "gdn_block_record_bytes",
     "gdn_verify_block",
     "gdn_commit",
+    "gdn_commit_verify",
     "gdn_record_status",
     "gdn_prefill_workspace_bytes",
     "gdn_prefill_chunked",
@@ -58,6 +59,8 @@ def _load() -> ctypes.CDLL:
     lib.gdn_verify_block.argtypes = [vp] * 6 + [i32, ctypes.c_int, sp, vp, vp, sz, vp]
     lib.gdn_commit.restype = ctypes.c_int
     lib.gdn_commit.argtypes = [vp, vp, vp, vp, sp, vp]
+    lib.gdn_commit_verify.restype = ctypes.c_int
+    lib.gdn_commit_verify.argtypes = [vp] * 9 + [i32, ctypes.c_int, sp, vp, vp, sz, vp]
     lib.gdn_record_status.restype = ctypes.c_int
     lib.gdn_record_status.argtypes = [vp, sp, ctypes.POINTER(i32), vp]
     lib.gdn_prefill_workspace_bytes.restype = sz
@@ -162,6 +165,23 @@ def gdn_commit(S, record, n_accepted, pos=None, stream=None) -> None:
                         _stream(stream))
     if rc != 0:
         raise GdnError(rc, "gdn_commit")
+
+
+def gdn_commit_verify(S, record_prev, n_accepted, q, k, v, g, beta, o, record_next, pos=None,
+                      stream=None) -> None:
+    """gdn_commit(S, record_prev, n_accepted, pos) then gdn_verify_block(S, q, k, v,
+    g, beta, o, record_next), in one pass over the state."""
+    shp = _shape_of(S)
+    T = _check_rows(shp, q, k, v, g, beta, o)
+    for name, x in (("n_accepted", n_accepted), ("pos", pos)):
+        if x is not None and (x.dtype != torch.int32 or tuple(x.shape) != (shp.B,)):
+            raise ValueError(f"{name} must be int32 [{shp.B}]")
+    rc = lib.gdn_commit_verify(_ptr(S), _ptr(record_prev), _ptr(n_accepted), _ptr(pos), _ptr(q), _ptr(k),
+                               _ptr(v), _ptr(g), _ptr(beta), T, _dt(q), ctypes.byref(shp), _ptr(o),
+                               _ptr(record_next), record_next.numel() * record_next.element_size(),
+                               _stream(stream))
+    if rc != 0:
+        raise GdnError(rc, "gdn_commit_verify")
 
 
 def gdn_record_status(record, S, stream=None) -> list[int]:

@@ -86,6 +86,24 @@ def test_commit_and_prefill_reject_bad_arguments(G):
     assert G.lib.gdn_record_status(FAKE, _shape(), None, None) == -1
 
 
+def test_commit_verify_rejects_bad_arguments(G):
+    FAKE2 = ctypes.c_void_p(1 << 24)
+    need = G.lib.gdn_block_record_bytes(_shape(), 8, 1)
+
+    def cv(S=FAKE, rprev=FAKE2, rnext=FAKE, T=8, dt=1, shp=None, nbytes=1 << 20, n=FAKE):
+        return G.lib.gdn_commit_verify(S, rprev, n, None, FAKE, FAKE, FAKE, FAKE, FAKE, T, dt,
+                                       shp or _shape(), FAKE, rnext, nbytes, None)
+    assert cv(S=None) == -1
+    assert cv(n=None) == -1
+    assert cv(rprev=FAKE) == -1                                  # the same record twice
+    assert cv(rprev=ctypes.c_void_p((1 << 20) + 4096)) == -1      # record_prev inside record_next
+    assert cv(rnext=ctypes.c_void_p((1 << 24) + 128)) == -1       # record_next over record_prev's header
+    assert cv(dt=4) == -1
+    assert cv(shp=_shape(dv=96)) == -2
+    assert cv(T=0) == -3 and cv(T=17) == -3
+    assert cv(nbytes=need - 1) == -4
+
+
 def test_record_size_accounts_for_payload(G):
     for (B, H, dk, dv, T, dt) in [(1, 2, 64, 64, 8, torch.float32), (48, 32, 128, 128, 8, torch.bfloat16),
                                   (3, 5, 128, 64, 16, torch.bfloat16), (2, 1, 64, 128, 1, torch.float32)]:
