@@ -47,6 +47,8 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--prefill-reps", type=int, default=20)
     p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--decode-steps", type=int, default=10000)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget-s", type=float, default=15.0)
     p.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -394,6 +396,8 @@ def main():
     result["copy_ceiling"] = copy_ceiling(dev)
     if not args.no_prefill:
         result["prefill"] = bench_prefill(args, G, dev)
+    if not args.no_decode:
+        result["decode"] = bench_decode(args, G, dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args)
     if args.copy_calibration_mib > 0:
@@ -566,6 +570,67 @@ def summarize_profiles(args):
         json.dump(summary, f, indent=1)
         f.write("\n")
     print(f"wrote {STATS_MD} and {TRAFFIC_JSON}")
+
+
+def bench_decode(args, G, dev):
+    """Plain decode, T = 1: one GDN layer, 32 heads, d = 128, bf16, a chain of
+    decode steps carrying the 2 MiB state, each step one gdn_commit_verify
+    (commit the previous token, n = 1, and verify the next).  Timed eagerly over
+    the whole chain and as a HIP graph of 100 chained steps replayed back to back.
+    The 2 MiB state stays in the caches between steps, so the effective rate is
+    not an HBM figure; the step is launch- and latency-bound."""
+    import torch
+
+    from speculative_verify_amd.inputs import make_inputs
+
+    B, H, L = 1, HEADS, args.decode_steps
+    x = make_inputs(B, H, DK, DV, L, seed=args.seed + 91, device=dev, device_gen=True)
+    S = x.S0.clone()
+    o = torch.empty(B, L, H, DV, dtype=torch.float32, device=dev)
+    recs = [G.new_record(S, 1, torch.bfloat16) for _ in range(2)]
+    one = torch.ones(B, dtype=torch.int32, device=dev)
+    sl = lambda a, t: a[:, t:t + 1]
+
+    def step(t):  # commits token t - 1, verifies token t
+        G.gdn_commit_verify(S, recs[(t + 1) % 2], one, sl(x.q, t), sl(x.k, t), sl(x.v, t), sl(x.g, t),
+                            sl(x.beta, t), sl(o, t), recs[t % 2])
+
+    G.gdn_verify_block(S, sl(x.q, 0), sl(x.k, 0), sl(x.v, 0), sl(x.g, 0), sl(x.beta, 0), sl(o, 0), recs[0])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(1, L):
+        step(t)
+    torch.cuda.synchronize()
+    eager_us = (time.perf_counter() - t0) / (L - 1) * 1e6
+
+    # A graph of 100 chained steps (an even count, so the records alternate
+    # consistently from one replay to the next).
+    GS = 100
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            for t in range(2, 2 + GS):
+                step(t)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    reps = max(1, (L - 1) // GS)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        graph.replay()
+    torch.cuda.synchronize()
+    graph_us = (time.perf_counter() - t0) / (reps * GS) * 1e6
+    nbytes = fused_bytes(B, H, DK, DV, 1, 1, 2)
+    return {"workload": f"plain decode: 1 layer x {H} heads, dk=dv={DK}, T=1, bf16, fp32 state (2 MiB), "
+                        f"{L} chained steps, one gdn_commit_verify per step",
+            "us_per_step_eager": round(eager_us, 2), "us_per_step_graph": round(graph_us, 2),
+            "tokens_per_s_graph": round(1e6 / graph_us, 1),
+            "algorithmic_bytes_per_step": nbytes,
+            "effective_GBs_graph": round(nbytes / (graph_us * 1e-6) / 1e9, 1),
+            "note": "state cache-resident between steps"}
 
 
 def bench_prefill(args, G, dev):
