@@ -627,7 +627,10 @@ struct alignas(16) ScanLds {
     uint8_t M[2][4 * C * C * 2];   // Linv hi, Linv lo, P hi, P lo
     uint8_t V[2][C * 32 * 2];      // the workgroup's 32 value columns, [t][32] bf16
     float G[2][256];               // gamma, e, beta (3 x 64), padded to 1 KiB
-    float O[C * kOStride];         // output staging, wave w owns columns 16w .. 16w + 15
+    float O[C * kOStride];         // output staging: token rows, the 32 value columns
+    // Partial K S^T exchange between the two key halves (4 waves x 4 tiles x 64
+    // lanes x 4); at dk = 128 the current stage's Q buffer, dead by then, holds it.
+    float Xch[DK == 128 ? 4 : 4 * 4 * 64 * 4];
 };
 
 typedef short v4s __attribute__((ext_vector_type(4)));
@@ -643,36 +646,49 @@ __device__ inline bf16x4 read_tr(const uint8_t *p) {
 
 __device__ inline bf16x8 lds16(const uint8_t *p) { return *reinterpret_cast<const bf16x8 *>(p); }
 
-// Store the wave's 16 staged output columns of one chunk as 64-byte row
-// segments (rows < n).  obase points at o for the chunk's first token and the
-// workgroup's first value column; ostride is one token.
+// Wave (g, kh) of a scan workgroup owns value rows 16 g .. 16 g + 15 (of the
+// workgroup's 32) and keys 64 kh .. 64 kh + 63 of their state; of the output
+// tiles it finalises tt = kh and kh + 2, i.e. tokens 32p + 8a + 4kh + r.
+
+// Store the wave's finished outputs of one chunk (its 32 tokens x 16 value
+// columns) from the staging buffer as 64-byte row segments (tokens < n).  obase
+// points at o for the chunk's first token and the workgroup's first value
+// column; ostride is one token.
 template <int DK>
-__device__ inline void scan_store_o(const ScanLds<DK> &sm, int n, int lane, int w, float *__restrict__ obase,
-                                    size_t ostride) {
+__device__ inline void scan_store_o(const ScanLds<DK> &sm, int n, int lane, int g, int kh,
+                                    float *__restrict__ obase, size_t ostride) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const int row = 16 * m + (lane >> 2), col = 16 * w + 4 * (lane & 3);
+    for (int i = 0; i < 2; ++i) {
+        const int j = 16 * i + (lane >> 2);                    // token index among the wave's 32
+        const int row = 32 * (j >> 4) + 8 * ((j >> 2) & 3) + 4 * kh + (j & 3);
+        const int col = 16 * g + 4 * (lane & 3);
         const float4 v4 = *reinterpret_cast<const float4 *>(&sm.O[row * kOStride + col]);
         if (row < n) *reinterpret_cast<float4 *>(obase + size_t(row) * ostride + col) = v4;
     }
 }
 
-// State-coupled products of one chunk for one wave's 16 value rows, from stage
-// s of the LDS buffers (the products of chunk_state, in the operand mapping
-// above).  The outputs are left in the staging buffer (this wave's columns).
+// State-coupled products of one chunk (the products of chunk_state) for wave
+// (g, kh), from stage s of the LDS buffers, in the operand mapping above.  st
+// holds the wave's quarter of the state: st[kt][r] is key 32 (KT/2) + 8 lg +
+// 4 (KT%2) + r of value row irow, KT = 4 kh + kt (dk = 128; dk = 64: 2 kh + kt).
+// The pair (g, 0), (g, 1) exchanges partial K S^T and Q S^T through LDS, with
+// the workgroup's barriers between.  Outputs stay in the staging buffer.
 template <int DK>
-__device__ inline void scan_chunk(ScanLds<DK> &sm, int s, float (&st)[DK / 16][4], int n, int lane, int w) {
-    constexpr int KT = DK / 16, KB = DK / 32;
+__device__ inline void scan_chunk(ScanLds<DK> &sm, int s, float (&st)[DK / 32][4], int n, int lane, int g,
+                                  int kh) {
+    constexpr int KTH = DK / 32;   // 16-key state tiles per key half
+    constexpr int KBH = DK / 64;   // 32-key contraction blocks per key half
     const int lr = lane & 15, lg = lane >> 4;
     const uint8_t *Kc = sm.K[s], *Qc = sm.Q[s], *Mc = sm.M[s];
     const float *Gc = sm.G[s];
+    float *xch = DK == 128 ? reinterpret_cast<float *>(sm.Q[s]) : sm.Xch;
 
-    // X = K S^T, Y = Q S^T (the split state dies here).
+    // Partial X = K S^T and Y = Q S^T over this wave's keys.
     f32x4 X[4], Y[4];
     {
-        Split8 sB[KB];
+        Split8 sB[KBH];
 #pragma unroll
-        for (int p = 0; p < KB; ++p) {
+        for (int p = 0; p < KBH; ++p) {
             const float x[8] = {st[2 * p][0], st[2 * p][1], st[2 * p][2], st[2 * p][3],
                                 st[2 * p + 1][0], st[2 * p + 1][1], st[2 * p + 1][2], st[2 * p + 1][3]};
             sB[p] = split8(x);
@@ -683,9 +699,10 @@ __device__ inline void scan_chunk(ScanLds<DK> &sm, int s, float (&st)[DK / 16][4
             Y[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
             const int t = tau(tt, lr);
 #pragma unroll
-            for (int p = 0; p < KB; ++p) {
-                const bf16x8 ka = lds16(Kc + kq_off<DK>(t, 4 * p + lg));
-                const bf16x8 qa = lds16(Qc + kq_off<DK>(t, 4 * p + lg));
+            for (int p = 0; p < KBH; ++p) {
+                const int piece = 4 * (KBH * kh + p) + lg;
+                const bf16x8 ka = lds16(Kc + kq_off<DK>(t, piece));
+                const bf16x8 qa = lds16(Qc + kq_off<DK>(t, piece));
                 X[tt] = mma(ka, sB[p].hi, X[tt]);
                 X[tt] = mma(ka, sB[p].lo, X[tt]);
                 Y[tt] = mma(qa, sB[p].hi, Y[tt]);
@@ -693,8 +710,42 @@ __device__ inline void scan_chunk(ScanLds<DK> &sm, int s, float (&st)[DK / 16][4
             }
         }
     }
+    // Exchange: every wave is done reading Q[s] (the exchange space at dk = 128);
+    // each wave posts its partial X, and its partial Y of the tiles its partner
+    // finalises into those tiles' output staging slots.
+    __syncthreads();
+    {
+        float *mine = xch + (2 * g + kh) * 1024 + lane * 4;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+            *reinterpret_cast<float4 *>(mine + tt * 256) = make_float4(X[tt][0], X[tt][1], X[tt][2], X[tt][3]);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int tt = (1 - kh) + 2 * hh, t0 = 32 * (tt >> 1) + 8 * lg + 4 * (tt & 1);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sm.O[(t0 + r) * kOStride + 16 * g + lr] = Y[tt][r];
+        }
+    }
+    __syncthreads();
+    {
+        const float *theirs = xch + (2 * g + (1 - kh)) * 1024 + lane * 4;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            const float4 o4 = *reinterpret_cast<const float4 *>(theirs + tt * 256);
+            X[tt][0] += o4.x;
+            X[tt][1] += o4.y;
+            X[tt][2] += o4.z;
+            X[tt][3] += o4.w;
+        }
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int tt = kh + 2 * hh, t0 = 32 * (tt >> 1) + 8 * lg + 4 * (tt & 1);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Y[tt][r] += sm.O[(t0 + r) * kOStride + 16 * g + lr];
+        }
+    }
     // R = diag(beta) (V - diag(gamma) X): lane (lr, lg) of tile tt = 2p + hh holds
-    // tokens t0 + r, t0 = 32p + 8lg + 4hh; v[t0 + r][16w + lr] by a transposed read.
+    // tokens t0 + r, t0 = 32p + 8lg + 4hh; v[t0 + r][16g + lr] by a transposed read.
     Split8 rB[2];
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
@@ -702,7 +753,7 @@ __device__ inline void scan_chunk(ScanLds<DK> &sm, int s, float (&st)[DK / 16][4
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             const int tt = 2 * p + hh, t0 = 32 * p + 8 * lg + 4 * hh;
-            const bf16x4 vt = read_tr(sm.V[s] + (t0 + (lr >> 2)) * 64 + 32 * w + 8 * (lr & 3));
+            const bf16x4 vt = read_tr(sm.V[s] + (t0 + (lr >> 2)) * 64 + 32 * g + 8 * (lr & 3));
             const float4 ga = *reinterpret_cast<const float4 *>(Gc + t0);
             const float4 be = *reinterpret_cast<const float4 *>(Gc + 128 + t0);
 #pragma unroll
@@ -711,7 +762,7 @@ __device__ inline void scan_chunk(ScanLds<DK> &sm, int s, float (&st)[DK / 16][4
         }
         rB[p] = split8(x);
     }
-    // D = Linv R (Linv is lower triangular: blocks p <= tt / 2).
+    // D = Linv R (both waves of the pair; Linv is lower triangular: p <= tt / 2).
     f32x4 D[4];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
@@ -743,33 +794,34 @@ __device__ inline void scan_chunk(ScanLds<DK> &sm, int s, float (&st)[DK / 16][4
         dB[p] = split8(x);
         eB[p] = split8(y);
     }
-    // O = diag(gamma) Y + P D, staged in LDS (this wave's 16 columns; the
-    // previous chunk's were stored from there before this chunk began).
+    // O = diag(gamma) Y + P D for this wave's tiles kh and kh + 2, into staging.
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
+    for (int hh = 0; hh < 2; ++hh) {
+        const int tt = kh + 2 * hh;
         const int t = tau(tt, lr), t0 = 32 * (tt >> 1) + 8 * lg + 4 * (tt & 1);
         const float4 ga = *reinterpret_cast<const float4 *>(Gc + t0);
         f32x4 Ot = Y[tt];
 #pragma unroll
         for (int r = 0; r < 4; ++r) Ot[r] *= (&ga.x)[r];
 #pragma unroll
-        for (int p = 0; p <= tt / 2; ++p) {
+        for (int p = 0; p <= hh; ++p) {   // p <= tt / 2 = hh
             Split8 a;
             a.hi = lds16(Mc + mat_off(2, t, 4 * p + lg));
             a.lo = lds16(Mc + mat_off(3, t, 4 * p + lg));
             Ot = mma3(a, dB[p], Ot);
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sm.O[(t0 + r) * kOStride + 16 * w + lr] = Ot[r];
+        for (int r = 0; r < 4; ++r) sm.O[(t0 + r) * kOStride + 16 * g + lr] = Ot[r];
     }
-    // S <- gamma_last S + K^T diag(e) D.  Tile kt's A operand is K^T at keys
-    // 32 (kt/2) + 8 (lr/4) + 4 (kt%2) + lr%4 (row lr) and tokens 32p + 8lg + {0..7}
-    // (slots), two transposed reads of 4 token rows each.
+    // S <- gamma_last S + K^T diag(e) D over this wave's keys.  Tile KT's A
+    // operand is K^T at keys 32 (KT/2) + 8 (lr/4) + 4 (KT%2) + lr%4 (row lr) and
+    // tokens 32p + 8lg + {0..7} (slots): two transposed reads of 4 token rows.
     const float glast = Gc[n - 1];
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
+    for (int kt = 0; kt < KTH; ++kt) {
+        const int KTg = KTH * kh + kt;
         f32x4 U = {0.f, 0.f, 0.f, 0.f};
-        const int piece = 4 * (kt >> 1) + (lr & 3), h8 = (kt & 1) << 3;
+        const int piece = 4 * (KTg >> 1) + (lr & 3), h8 = (KTg & 1) << 3;
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
             const int ta = 32 * p + 8 * lg + (lr >> 2);
@@ -784,15 +836,16 @@ __device__ inline void scan_chunk(ScanLds<DK> &sm, int s, float (&st)[DK / 16][4
 }
 
 template <int DK, int DV>
-__global__ __launch_bounds__(128) void prefill_scan_kernel(
+__global__ __launch_bounds__(256) void prefill_scan_kernel(
     float *__restrict__ S, const __hip_bfloat16 *__restrict__ q, const __hip_bfloat16 *__restrict__ k,
     const __hip_bfloat16 *__restrict__ v, int L, int H, int nchunks, const float *__restrict__ ws,
     float *__restrict__ o) {
-    constexpr int RS = 32;                 // value rows per workgroup (2 waves of 16)
+    constexpr int RS = 32;                  // value rows per workgroup
+    constexpr int NW = 4;                   // waves: 2 row groups x 2 key halves
     constexpr int SLICES = DV / RS;
-    constexpr int KT = DK / 16;
+    constexpr int KTH = DK / 32;            // 16-key state tiles per wave
     constexpr int NKQ = C * DK * 2 / 1024;  // 1 KiB blocks of a key or query chunk
-    static_assert(SLICES * RS == DV && NKQ % 2 == 0, "tiling");
+    static_assert(SLICES * RS == DV && NKQ % NW == 0, "tiling");
 
     __shared__ ScanLds<DK> sm;
 
@@ -814,14 +867,17 @@ __global__ __launch_bounds__(128) void prefill_scan_kernel(
     const int tid = threadIdx.x, lane = tid & 63;
     const int lr = lane & 15, lg = lane >> 4;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int irow = slice * RS + w * 16 + lr;
+    const int g = w >> 1, kh = w & 1;        // row group, key half
+    const int irow = slice * RS + 16 * g + lr;
 
-    // State in registers: st[kt][r] = S[irow][32 (kt/2) + 8 lg + 4 (kt%2) + r].
+    // State quarter in registers: st[kt][r] = S[irow][32 (KT/2) + 8 lg + 4 (KT%2) + r],
+    // KT = KTH kh + kt.
     float *Srow = S + (size_t(bh) * DV + irow) * DK;
-    float st[KT][4];
+    float st[KTH][4];
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-        const float4 s4 = *reinterpret_cast<const float4 *>(Srow + 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1));
+    for (int kt = 0; kt < KTH; ++kt) {
+        const int KT = KTH * kh + kt;
+        const float4 s4 = *reinterpret_cast<const float4 *>(Srow + 32 * (KT >> 1) + 8 * lg + 4 * (KT & 1));
         st[kt][0] = s4.x;
         st[kt][1] = s4.y;
         st[kt][2] = s4.z;
@@ -835,26 +891,23 @@ __global__ __launch_bounds__(128) void prefill_scan_kernel(
     const size_t kstride = size_t(H) * DK, vstride = size_t(H) * DV;
 
     // Copy chunk cn's operands into stage cn & 1.  Wave w takes the 1 KiB blocks
-    // w, w + 2, ...  Full chunks use uniform bases and per-lane offsets computed
+    // w, w + 4, ...  Full chunks use uniform bases and per-lane offsets computed
     // once; a partial last chunk clamps each lane's row to the last token (finite
     // data that beta = e = 0 cancels; those outputs are not stored).
     constexpr int RPB = 1024 / (2 * DK);      // key rows per 1 KiB block
     const uint32_t kstride_b = uint32_t(kstride) * 2, vstride_b = uint32_t(vstride) * 2;
-    auto kq_piece = [&](int u) {             // swizzled piece of this lane in K/Q block 2u + w
-        const int row = (2 * u + w) * RPB + lane / (64 / RPB), slot = lane % (64 / RPB);
+    auto kq_piece = [&](int blk) {           // swizzled piece of this lane in K/Q block blk
+        const int row = blk * RPB + lane / (64 / RPB), slot = lane % (64 / RPB);
         return DK == 128 ? (slot ^ swz16(row)) : (slot ^ swz8(row));
     };
-    // Per-lane offsets within a block (the block's own offset is uniform).  The
-    // swizzles depend on the row modulo 32, so the K/Q pattern repeats every 4
-    // blocks of a wave and the matrices' every 2.
-    uint32_t vo_kq[4], vo_m[2];
+    uint32_t vo_kq[NKQ / NW], vo_m[32 / NW];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-        vo_kq[j] = uint32_t(lane / (64 / RPB)) * kstride_b + 16u * uint32_t(kq_piece(j));
+    for (int u = 0; u < NKQ / NW; ++u)
+        vo_kq[u] = uint32_t(lane / (64 / RPB)) * kstride_b + 16u * uint32_t(kq_piece(NW * u + w));
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int mrow = ((2 * j + w) & 7) * 8 + (lane >> 3);  // row of block 2j + w in its matrix
-        vo_m[j] = uint32_t(lane >> 3) * 128u + 16u * uint32_t((lane & 7) ^ swz8(mrow));
+    for (int u = 0; u < 32 / NW; ++u) {
+        const int blk = NW * u + w, mrow = (blk & 7) * 8 + (lane >> 3);  // row of the block in its matrix
+        vo_m[u] = uint32_t(lane >> 3) * 128u + 16u * uint32_t((lane & 7) ^ swz8(mrow));
     }
     const uint32_t vo_v = uint32_t(lane >> 2) * vstride_b + 16u * uint32_t(lane & 3);
     const uint32_t vo_g = 16u * uint32_t(min(lane, 3 * C / 4 - 1));
@@ -868,40 +921,28 @@ __global__ __launch_bounds__(128) void prefill_scan_kernel(
             const uint8_t *qc = reinterpret_cast<const uint8_t *>(qb + size_t(c0) * kstride);
             const uint8_t *vc = reinterpret_cast<const uint8_t *>(vb + size_t(c0) * vstride);
 #pragma unroll
-            for (int u = 0; u < NKQ / 2; ++u) {
-                const int blk = 2 * u + w;
+            for (int u = 0; u < NKQ / NW; ++u) {
+                const int blk = NW * u + w;
                 const size_t boff = size_t(blk * RPB) * kstride_b;
-                dma16s(kc + boff, vo_kq[u & 3], lk + blk * 1024);
-                dma16s(qc + boff, vo_kq[u & 3], lq + blk * 1024);
+                dma16s(kc + boff, vo_kq[u], lk + blk * 1024);
+                dma16s(qc + boff, vo_kq[u], lq + blk * 1024);
             }
-#pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                const int blk = 2 * u + w;
-                dma16s(rec + blk * 1024, vo_m[u & 1], lm + blk * 1024);
-            }
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int blk = 2 * u + w;
-                dma16s(vc + size_t(16 * blk) * vstride_b, vo_v, lv + blk * 1024);
-            }
+            dma16s(vc + size_t(16 * w) * vstride_b, vo_v, lv + w * 1024);
         } else {
 #pragma unroll
-            for (int u = 0; u < NKQ / 2; ++u) {
-                const int blk = 2 * u + w, row = blk * RPB + lane / (64 / RPB);
-                const size_t off = size_t(min(c0 + row, L - 1)) * kstride + 8 * kq_piece(u);
+            for (int u = 0; u < NKQ / NW; ++u) {
+                const int blk = NW * u + w, row = blk * RPB + lane / (64 / RPB);
+                const size_t off = size_t(min(c0 + row, L - 1)) * kstride + 8 * kq_piece(blk);
                 dma16(kb + off, lk + blk * 1024);
                 dma16(qb + off, lq + blk * 1024);
             }
+            const int row = 16 * w + (lane >> 2);
+            dma16(vb + size_t(min(c0 + row, L - 1)) * vstride + 8 * (lane & 3), lv + w * 1024);
+        }
 #pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                const int blk = 2 * u + w;
-                dma16s(rec + blk * 1024, vo_m[u & 1], lm + blk * 1024);
-            }
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int blk = 2 * u + w, row = 16 * blk + (lane >> 2);
-                dma16(vb + size_t(min(c0 + row, L - 1)) * vstride + 8 * (lane & 3), lv + blk * 1024);
-            }
+        for (int u = 0; u < 32 / NW; ++u) {
+            const int blk = NW * u + w;
+            dma16s(rec + blk * 1024, vo_m[u], lm + blk * 1024);
         }
         if (w == 0) dma16s(rec + kPrepMatBytes, vo_g, lds_addr(sm.G[s]));
     };
@@ -918,20 +959,20 @@ __global__ __launch_bounds__(128) void prefill_scan_kernel(
         __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) expcnt(7) lgkmcnt(0)
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        if (c > 0) scan_store_o<DK>(sm, C, lane, w, ob + size_t(c0 - C) * ostride, ostride);
+        if (c > 0) scan_store_o<DK>(sm, C, lane, g, kh, ob + size_t(c0 - C) * ostride, ostride);
         if (c + 1 < nchunks) issue(c + 1);
-        // The staged outputs were read (in-order LDS per wave) before this chunk
-        // overwrites them; the compiler barrier keeps that order.
         asm volatile("" ::: "memory");
-        scan_chunk<DK>(sm, c & 1, st, n, lane, w);
+        scan_chunk<DK>(sm, c & 1, st, n, lane, g, kh);
     }
     asm volatile("" ::: "memory");
-    scan_store_o<DK>(sm, L - (nchunks - 1) * C, lane, w, ob + size_t(nchunks - 1) * C * ostride, ostride);
+    scan_store_o<DK>(sm, L - (nchunks - 1) * C, lane, g, kh, ob + size_t(nchunks - 1) * C * ostride, ostride);
 
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
-        *reinterpret_cast<float4 *>(Srow + 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1)) =
+    for (int kt = 0; kt < KTH; ++kt) {
+        const int KT = KTH * kh + kt;
+        *reinterpret_cast<float4 *>(Srow + 32 * (KT >> 1) + 8 * lg + 4 * (KT & 1)) =
             make_float4(st[kt][0], st[kt][1], st[kt][2], st[kt][3]);
+    }
 }
 
 template <int DK, int DV>
@@ -948,7 +989,7 @@ hipError_t launch_dk_dv(float *S, const void *q, const void *k, const void *v, c
                            qq, kk, g, beta, L, s.H, nchunks, static_cast<float *>(ws));
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((prefill_scan_kernel<DK, DV>), dim3(unsigned(heads * (DV / 32))), dim3(128), 0, st,
+        hipLaunchKernelGGL((prefill_scan_kernel<DK, DV>), dim3(unsigned(heads * (DV / 32))), dim3(256), 0, st,
                            S, qq, kk, vv, L, s.H, nchunks, static_cast<const float *>(ws), o);
         return hipGetLastError();
     }
