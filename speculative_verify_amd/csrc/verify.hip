@@ -82,7 +82,12 @@ __device__ inline bf16x8 xrow_bf16(const uint8_t *Xb, int x, int p, int lg) {
 // the commit kernel does (same checks, error bits, flags and pos), applying the
 // rank-n update to each state tile as it arrives and writing S_n back; then
 // verify the new block from S_n.  Each (instance, head) reads its state once.
-template <int DK, int DV, typename TIn, int MT, bool FUSED>
+//
+// NT = 16-row tiles per wave: 4 (a workgroup covers a head's dv rows), or 1 for
+// few heads (a workgroup covers 32 rows, dv / 32 workgroups per head, each
+// computing the head's block coefficients itself): four times the workgroups,
+// a quarter of the state per wave.
+template <int DK, int DV, typename TIn, int MT, bool FUSED, int NT>
 __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void verify_kernel(
     float *__restrict__ S, const TIn *__restrict__ q, const TIn *__restrict__ k,
     const TIn *__restrict__ v, const float *__restrict__ g, const float *__restrict__ beta,
@@ -90,7 +95,9 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void ve
     const int32_t *__restrict__ n_acc, int32_t *__restrict__ pos) {
     constexpr int NW = DV / 64;      // waves per workgroup
     constexpr int NTH = 64 * NW;     // threads
-    constexpr int NT = 4;            // 16-row MFMA tiles per wave (64 rows)
+    constexpr int RW = 16 * NT;      // value rows per wave
+    constexpr int RS = NW * RW;      // value rows per workgroup
+    constexpr int SLICES = DV / RS;  // workgroups per head
     constexpr int KM = DK / 16;      // 16-key groups (4 keys per lane group)
     constexpr int XR = 16 * MT;      // rows of X
     constexpr int XS = DK + 4;       // LDS row stride of the fp32 X, floats
@@ -103,14 +110,14 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void ve
     // bf16 inputs: 1 KiB copy blocks of K (and of Q) and of V.
     constexpr int NBK = TM * DK * 2 / 1024, NBV = TM * DV * 2 / 1024;
     constexpr int NSTATE = NT * KM;  // state loads per thread
-    static_assert(NW * 64 == DV && KH * NW == KM, "shape");
+    static_assert(NW * 64 == DV && KH * NW == KM && SLICES * RS == DV && RS % kCommitRows == 0, "shape");
     static_assert(!kBf16 || (NBK >= 1 && NBV >= 1 && NSTATE <= 63), "copy blocks");
 
     __shared__ __attribute__((aligned(16))) float X[kBf16 ? 4 : XR * XS];
     __shared__ __attribute__((aligned(16))) uint8_t Xb[kBf16 ? XR * 2 * DK : 16];
     __shared__ __attribute__((aligned(16))) uint8_t Vb[kBf16 ? TM * DV * 2 : 16];   // bf16 [TM][DV]
     __shared__ __attribute__((aligned(16))) float Vs[kBf16 ? 4 : TM * DV];          // fp32 [TM][DV]
-    __shared__ float P[XR][DV + 1];               // [K;Q] S^T: rows x, columns value row
+    __shared__ float P[XR][RS + 1];               // [K;Q] S^T: rows x, columns value row (local)
     __shared__ float gpart[NW][XR][XR + 1];       // per-wave partial Gram matrices
     __shared__ float coefM[TM][TM + 1], coefN[TM][TM + 1];
     __shared__ float Gs[TM], gam[TM], bs[TM];
@@ -122,11 +129,13 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void ve
     __shared__ __attribute__((aligned(16))) uint8_t kraw[FUSED ? CR * DK * 4 : 16];
     __shared__ __attribute__((aligned(16))) float gprev[FUSED ? 64 : 4];
 
-    const int bh = blockIdx.x;
+    const int bh = blockIdx.x / SLICES, slice = blockIdx.x - bh * SLICES;
     const int b = bh / H, h = bh - b * H;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 15, lg = lane >> 4;
+    const int rbase = slice * RS;                 // first value row of the workgroup
+    const int fl0 = rbase / kCommitRows;          // its first pending flag (commit slice)
     const RecLayout RL = rec_layout(B, T, H, DK, DV, int(sizeof(TIn)));
 
     // FUSED: the pending block's status (uniform over the workgroup).  cn rows
@@ -151,7 +160,7 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void ve
                 const uint32_t *fl = reinterpret_cast<const uint32_t *>(rprev + RLp.flags) + size_t(bh) * kCommitSlices;
                 bool valid = true;
 #pragma unroll
-                for (int sl = 0; sl < DV / kCommitRows; ++sl) valid = valid && fl[sl] == kRecValid;
+                for (int sl = 0; sl < RS / kCommitRows; ++sl) valid = valid && fl[fl0 + sl] == kRecValid;
                 const int n = n_acc[b];
                 if (!valid) {
                     cerr = GDN_REC_NO_BLOCK;
@@ -252,8 +261,8 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void ve
     //    tiles in flight and issues the next after writing one back, so that its
     //    reads and write-backs share the memory system instead of queueing as a
     //    read phase followed by a write phase.
-    constexpr int NPRE = FUSED ? 2 : NT;   // tiles loaded up front
-    const float *Sw = S + (size_t(bh) * DV + 64 * w + lr) * DK + 4 * lg;
+    constexpr int NPRE = FUSED ? (NT < 2 ? NT : 2) : NT;   // tiles loaded up front
+    const float *Sw = S + (size_t(bh) * DV + rbase + RW * w + lr) * DK + 4 * lg;
     float4 sreg[NT][KM];
     auto load_tile = [&](int nt) {
 #pragma unroll
@@ -300,13 +309,16 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void ve
     float gam_n = 1.f;
     if constexpr (FUSED) {
         if (cn > 0) {
-            // exp(G_n - G_j) delta_j for this thread's value row (rows 64w .. 64w + 63
-            // belong to wave w, which is the only reader of them).
+            // exp(G_n - G_j) delta_j for the wave's own value rows (lane < RW:
+            // row rbase + RW w + lane; wave w is the only reader of them).
             const float Gn = gprev[cn - 1];
             gam_n = expf(Gn);
+            if (lane < RW) {
+                const int row = rbase + RW * w + lane;
 #pragma unroll
-            for (int j = 0; j < CR; ++j)
-                if (j < cn) cdraw[j * DV + tid] *= expf(Gn - gprev[j]);
+                for (int j = 0; j < CR; ++j)
+                    if (j < cn) cdraw[j * DV + row] *= expf(Gn - gprev[j]);
+            }
         }
     }
     if (w == 0) {
@@ -324,10 +336,10 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void ve
             Gs[lane] = Gp;
             gam[lane] = expf(Gp);
             bs[lane] = bv;
-            reinterpret_cast<float *>(rec + RL.G)[size_t(b * T + lane) * H + h] = Gp;
+            if (slice == 0) reinterpret_cast<float *>(rec + RL.G)[size_t(b * T + lane) * H + h] = Gp;
         }
     }
-    if constexpr (kBf16) {
+    if (kBf16 && slice == 0) {
         // The block's keys into the record, from the LDS copy (unswizzled).
         for (int c = tid; c < T * DK / 8; c += NTH) {
             const int r = c / (DK / 8), piece = c - r * (DK / 8);
@@ -413,7 +425,7 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void ve
             if (cn > 0) {
                 // S_n = exp(G_n) S + sum_{j < n} exp(G_n - G_j) delta_j k_j^T for this
                 // tile (row 64w + 16nt + lr, keys 16m + 4lg + {0..3}), written back.
-                const int row = 64 * w + 16 * nt + lr;
+                const int row = rbase + RW * w + 16 * nt + lr;
 #pragma unroll
                 for (int m = 0; m < KM; ++m) {
                     sreg[nt][m].x *= gam_n;
@@ -513,15 +525,17 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void ve
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) P[16 * mt + 4 * lg + r][64 * w + 16 * nt + lr] = acc[mt][r];
+            for (int r = 0; r < 4; ++r) P[16 * mt + 4 * lg + r][RW * w + 16 * nt + lr] = acc[mt][r];
     }
-    // P columns 64w..64w+63 are this wave's own; its LDS operations complete in
-    // order, and the compiler-only barrier keeps the compiler from reordering them.
+    // P columns RW w .. RW w + RW - 1 are this wave's own; its LDS operations
+    // complete in order, and the compiler-only barrier keeps the compiler from
+    // reordering them.
     asm volatile("" ::: "memory");
 
-    // Value rows (one per thread): forward substitution for delta, then outputs.
-    {
-        const int i = tid;
+    // Value rows (one per lane, lane < RW of each wave): forward substitution for
+    // delta, then outputs.
+    if (lane < RW) {
+        const int li = RW * w + lane, i = rbase + li;
         float *Drec = reinterpret_cast<float *>(rec + RL.delta);
         float d[TM];
 #pragma unroll
@@ -532,11 +546,11 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void ve
                     vt = bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(Vb)[t * DV + i]);
                 else
                     vt = Vs[t * DV + i];
-                float dt = bs[t] * (vt - gam[t] * P[t][i]);
+                float dt = bs[t] * (vt - gam[t] * P[t][li]);
 #pragma unroll
                 for (int j = 0; j < t; ++j) dt -= coefM[t][j] * d[j];
                 d[t] = dt;
-                float ot = gam[t] * P[TM + t][i];
+                float ot = gam[t] * P[TM + t][li];
 #pragma unroll
                 for (int j = 0; j <= t; ++j) ot += coefN[t][j] * d[j];
                 const size_t idx = (size_t(b * T + t) * H + h) * DV + i;
@@ -549,9 +563,9 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void ve
     if constexpr (FUSED) {
         // Retire the committed block (every thread read the flags above, before
         // the barriers since) or report why nothing was committed.
-        if (cok && tid < DV / kCommitRows)
-            reinterpret_cast<uint32_t *>(rprev + RLp.flags)[size_t(bh) * kCommitSlices + tid] = 0u;
-        if (tid == 0 && h == 0) {
+        if (cok && tid < RS / kCommitRows)
+            reinterpret_cast<uint32_t *>(rprev + RLp.flags)[size_t(bh) * kCommitSlices + fl0 + tid] = 0u;
+        if (tid == 0 && h == 0 && slice == 0) {
             if (cok && pos) pos[b] += cn;
             if (cerr) atomicOr(&reinterpret_cast<RecCtrl *>(rprev + 256)[b].err, cerr);
         }
@@ -559,10 +573,10 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void ve
 
     // Mark the block pending for every commit workgroup of this head, clear the
     // instance's error bits; the header describes the record.
-    if (tid < DV / kCommitRows)
-        reinterpret_cast<uint32_t *>(rec + RL.flags)[size_t(bh) * kCommitSlices + tid] = kRecValid;
-    if (tid == 0 && h == 0) reinterpret_cast<RecCtrl *>(rec + RL.ctrl)[b].err = 0u;
-    if (tid == 0 && bh == 0) {
+    if (tid < RS / kCommitRows)
+        reinterpret_cast<uint32_t *>(rec + RL.flags)[size_t(bh) * kCommitSlices + fl0 + tid] = kRecValid;
+    if (tid == 0 && h == 0 && slice == 0) reinterpret_cast<RecCtrl *>(rec + RL.ctrl)[b].err = 0u;
+    if (tid == 0 && bh == 0 && slice == 0) {
         RecHeader *hd = reinterpret_cast<RecHeader *>(rec);
         hd->T = T;
         hd->B = B;
@@ -574,22 +588,40 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void ve
     }
 }
 
+constexpr unsigned kFewVerifyHeads = 256;  // fewer (instance, head) pairs: 4x the workgroups
+
 template <int DK, int DV, typename TIn, bool FUSED>
 hipError_t launch_t(float *S, const void *q, const void *k, const void *v, const float *g,
                     const float *beta, int T, const gdn_shape &s, float *o, void *rec, void *rprev,
                     const int32_t *n_acc, int32_t *pos, hipStream_t st) {
-    const dim3 grid(unsigned(s.B) * unsigned(s.H)), block(DV);
+    const unsigned heads = unsigned(s.B) * unsigned(s.H);
+    const dim3 block(DV);
     auto *qq = static_cast<const TIn *>(q);
     auto *kk = static_cast<const TIn *>(k);
     auto *vv = static_cast<const TIn *>(v);
     auto *rr = static_cast<uint8_t *>(rec);
     auto *rp = static_cast<uint8_t *>(rprev);
-    if (T <= 8)
-        hipLaunchKernelGGL((verify_kernel<DK, DV, TIn, 1, FUSED>), grid, block, 0, st, S, qq, kk, vv, g,
-                           beta, T, s.B, s.H, o, rr, rp, n_acc, pos);
-    else
-        hipLaunchKernelGGL((verify_kernel<DK, DV, TIn, 2, FUSED>), grid, block, 0, st, S, qq, kk, vv, g,
-                           beta, T, s.B, s.H, o, rr, rp, n_acc, pos);
+    // Few heads (fewer workgroups than compute units): 32 value rows per
+    // workgroup; otherwise a whole head per workgroup.
+    if (heads < kFewVerifyHeads) {
+        constexpr int NTF = 128 / DV;  // tiles per wave for 32-row workgroups
+        static_assert(NTF * 16 * (DV / 64) == 32, "few-heads workgroups cover 32 value rows");
+        const dim3 grid(heads * unsigned(DV / 32));
+        if (T <= 8)
+            hipLaunchKernelGGL((verify_kernel<DK, DV, TIn, 1, FUSED, NTF>), grid, block, 0, st, S, qq, kk, vv, g,
+                               beta, T, s.B, s.H, o, rr, rp, n_acc, pos);
+        else
+            hipLaunchKernelGGL((verify_kernel<DK, DV, TIn, 2, FUSED, NTF>), grid, block, 0, st, S, qq, kk, vv, g,
+                               beta, T, s.B, s.H, o, rr, rp, n_acc, pos);
+    } else {
+        const dim3 grid(heads);
+        if (T <= 8)
+            hipLaunchKernelGGL((verify_kernel<DK, DV, TIn, 1, FUSED, 4>), grid, block, 0, st, S, qq, kk, vv, g,
+                               beta, T, s.B, s.H, o, rr, rp, n_acc, pos);
+        else
+            hipLaunchKernelGGL((verify_kernel<DK, DV, TIn, 2, FUSED, 4>), grid, block, 0, st, S, qq, kk, vv, g,
+                               beta, T, s.B, s.H, o, rr, rp, n_acc, pos);
+    }
     return hipGetLastError();
 }
 
