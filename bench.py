@@ -666,7 +666,7 @@ def bench_prefill(args, G, dev):
     gbs = by / (avg * 1e-3) / 1e9
     return {"workload": f"chunked prefill: {PF_B} layer x {PF_H} heads, dk=dv={DK}, L={PF_L}, chunk {PF_C}, "
                         f"bf16 in, fp32 state, cold caches",
-            "schedule": "two-pass (chunk prep, then scan)" if need else "one-pass",
+            "schedule": "two-phase (chunk prep, scan; prep of each segment beside the scan of the previous)" if need else "one-pass",
             "workspace_bytes": need,
             "tokens_per_s": round(PF_L / (avg * 1e-3), 1), "avg_launch_us": round(avg * 1e3, 2),
             "mfma": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_MFMA_PEAK_TFLOPS,

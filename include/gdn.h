@@ -181,11 +181,14 @@ int gdn_record_status(const void *record, const gdn_shape *shp, int32_t *host_er
                       void *hip_stream);
 
 /*
- * Bytes of workspace with which gdn_prefill_chunked runs its two-pass schedule
- * for prompt length L: a parallel pass builds every chunk's state-independent
- * quantities first, so the sequential chunk scan carries only state-coupled work.
- * It pays off for few (instance, head) pairs (long scans, idle compute units);
- * 0 means the one-pass schedule is used for this shape and no workspace helps.
+ * Bytes of workspace with which gdn_prefill_chunked runs its two-phase schedule
+ * for prompt length L: a parallel prep builds every chunk's state-independent
+ * quantities into the workspace, so the sequential chunk scan carries only
+ * state-coupled work.  The prompt's chunks are cut into segments; the prep of
+ * each segment runs on the compute units the scan of the previous one leaves
+ * idle (one launch per segment, on the caller's stream).  It pays off for few
+ * (instance, head) pairs (long scans, idle compute units); 0 means the one-pass
+ * schedule is used for this shape and no workspace helps.
  */
 size_t gdn_prefill_workspace_bytes(const gdn_shape *shp, int32_t L, int32_t chunk);
 
@@ -204,7 +207,7 @@ size_t gdn_prefill_workspace_bytes(const gdn_shape *shp, int32_t L, int32_t chun
  *            no-op); the last chunk may be partial.
  *   chunk    GDN_PREFILL_CHUNK.
  *   ws       optional device workspace (16-byte aligned).  With at least
- *            gdn_prefill_workspace_bytes(...) bytes the two-pass schedule runs;
+ *            gdn_prefill_workspace_bytes(...) bytes the two-phase schedule runs;
  *            with NULL or fewer bytes the one-pass schedule runs.  Results agree
  *            within rounding either way.
  *

@@ -72,6 +72,30 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ inline float bf16_bits_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// Split eight fp32 values into high and low bf16 parts, both rounded to nearest
+// even: hi = bf16(x), lo = bf16(x - hi), so x = hi + lo + r with
+// |r| <= 2^-17 |x| (outside the subnormal range).  Two values are converted per
+// instruction; hi is widened back from its packed bits (a shift for the low
+// half, a mask for the high half) instead of being converted again.
+__device__ inline void split8_bf16(const float (&x)[8], bf16x8 &hi, bf16x8 &lo) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 h, l;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t u = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{x[2 * i], x[2 * i + 1]}), bf16x2));
+        h[i] = u;
+        const float h0 = __uint_as_float(u << 16), h1 = __uint_as_float(u & 0xffff0000u);
+        l[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{x[2 * i] - h0, x[2 * i + 1] - h1}), bf16x2));
+    }
+    hi = __builtin_bit_cast(bf16x8, h);
+    lo = __builtin_bit_cast(bf16x8, l);
+}
+
 // Load 8 consecutive input elements (16 B of bf16 or 32 B of fp32) as fp32.
 template <typename TIn> struct In8;
 template <> struct In8<float> {
@@ -113,20 +137,29 @@ template <> __device__ inline float load1<__hip_bfloat16>(const __hip_bfloat16 *
 // does not wait for all of them before every LDS read; the kernels wait for
 // them explicitly (s_waitcnt vmcnt) before reading what they copied.
 __device__ inline void dma16(const void *src, uint32_t lds_base) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(src)
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(src)
                  : "memory", "m0");
 }
 
 // 4 bytes per lane (global_load_lds_dword): lane l's word lands at lds_base + 4 l.
 __device__ inline void dma4(const void *src, uint32_t lds_base) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_base), "v"(src)
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(src)
                  : "memory", "m0");
 }
 
 // The same with a uniform 64-bit base in SGPRs and a 32-bit per-lane byte
 // offset (the saddr form): no per-lane 64-bit address arithmetic.
 __device__ inline void dma16s(const void *sbase, uint32_t voff, uint32_t lds_base) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_base), "v"(voff), "s"(sbase)
+    // Both are wave-uniform by contract; readfirstlane keeps them in SGPRs where
+    // the compiler cannot prove it (free when they already are).
+    // (readfirstlane returns int: both halves go back through uint32_t before
+    // widening, or a low word with bit 31 set would sign-extend over the high.)
+    const uint64_t sb = reinterpret_cast<uint64_t>(sbase);
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(sb >> 32)));
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(sb & 0xffffffffu)));
+    const uint64_t sbu = (uint64_t(hi) << 32) | uint64_t(lo);
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(__builtin_amdgcn_readfirstlane(lds_base)),
+                 "v"(voff), "s"(sbu)
                  : "memory", "m0");
 }
 

@@ -31,10 +31,14 @@
 // Two schedules:
 //  - one pass (many heads): one workgroup per head builds and consumes each
 //    chunk's quantities itself;
-//  - two passes (few heads, where the chunk scan's latency dominates): a prep
-//    kernel builds Linv, P and the gates of every chunk in parallel into a
-//    workspace, and a scan kernel walks the chunks doing only state-coupled
-//    work, with the next chunk's operands prefetched in registers.
+//  - two phases (few heads, where the chunk scan's latency dominates): a prep
+//    builds Linv, P and the gates of every chunk in parallel into a
+//    workspace, and a scan walks the chunks doing only state-coupled work,
+//    with the next chunk's operands copied into LDS one chunk ahead.  The
+//    chunks are cut into segments and each segment's prep runs beside the
+//    previous segment's scan, on the compute units the scan leaves idle.
+#include <algorithm>
+
 #include "gdn_internal.h"
 
 namespace gdn {
@@ -42,8 +46,6 @@ namespace {
 
 constexpr int C = GDN_PREFILL_CHUNK;
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 __device__ inline f32x4 mma(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -55,12 +57,7 @@ struct Split8 {
 
 __device__ inline Split8 split8(const float (&x)[8]) {
     Split8 s;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const __bf16 h = static_cast<__bf16>(x[e]);
-        s.hi[e] = h;
-        s.lo[e] = static_cast<__bf16>(x[e] - static_cast<float>(h));
-    }
+    split8_bf16(x, s.hi, s.lo);
     return s;
 }
 
@@ -109,11 +106,11 @@ struct alignas(16) PrepSmem {
     float gam[C], ee[C], bet[C], G[C];
 };
 
-// Workspace record of one (instance, head, chunk) in the two-pass schedule.
+// Workspace record of one (instance, head, chunk) in the two-phase schedule.
 // Linv and P as bf16 (hi, lo) pairs: four [C][C] bf16 arrays, then gam, ee, bet.
 constexpr size_t kPrepMatBytes = 4 * C * C * sizeof(__bf16);
 constexpr size_t kPrepBytes = (kPrepMatBytes + 3 * C * sizeof(float) + 255) & ~size_t(255);
-constexpr int kFewHeads = 256;  // fewer (instance, head) pairs than this: two passes
+constexpr int kFewHeads = 256;  // fewer (instance, head) pairs than this: two phases
 
 // Keys and queries of one chunk as raw 16-byte pieces: piece u of thread tid is
 // row t = (tid + u NT) / (DK / 8), columns col .. col + 7.
@@ -536,17 +533,15 @@ __global__ __launch_bounds__(64 * NWS) void prefill_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Two passes, first: one workgroup per (instance, head, chunk) builds Linv, P and
-// the gates of its chunk and writes them to the workspace.
+// Two-phase schedule, prep: a workgroup builds Linv, P and the gates of one
+// (instance, head, chunk) and writes them to that chunk's workspace record.
 // ---------------------------------------------------------------------------
 template <int DK>
-__global__ __launch_bounds__(256) void prefill_prep_kernel(
-    const __hip_bfloat16 *__restrict__ q, const __hip_bfloat16 *__restrict__ k,
-    const float *__restrict__ g, const float *__restrict__ beta, int L, int H, int nchunks,
-    float *__restrict__ ws) {
+__device__ __forceinline__ void prep_unit(PrepSmem<DK> &sm, const __hip_bfloat16 *__restrict__ q,
+                                 const __hip_bfloat16 *__restrict__ k, const float *__restrict__ g,
+                                 const float *__restrict__ beta, int L, int H, int nchunks,
+                                 uint8_t *__restrict__ ws, int bh, int c) {
     constexpr int NWS = 4, NT = 256;
-    __shared__ PrepSmem<DK> sm;
-    const int bh = blockIdx.x / nchunks, c = blockIdx.x - bh * nchunks;
     const int b = bh / H, h = bh - b * H;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -563,7 +558,7 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
     __syncthreads();
     chunk_prep<DK, NWS>(sm, tid, w, lane);
     // Linv hi, Linv lo, P hi, P lo as dense bf16 [C][C], then gam, ee, bet.
-    uint8_t *out = reinterpret_cast<uint8_t *>(ws) + (size_t(bh) * nchunks + c) * kPrepBytes;
+    uint8_t *out = ws + (size_t(bh) * nchunks + c) * kPrepBytes;
     for (int idx = tid; idx < C * C / 8; idx += NT) {
         const int t = idx / (C / 8), j8 = (idx - t * (C / 8)) * 8;
         Split8 ls, ps;
@@ -583,8 +578,8 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Two passes, second: one workgroup per (instance, head, 32 value rows) walks
-// the chunks doing only the state-coupled products.  Each chunk's operands
+// Two phases, scan: one workgroup per (instance, head, 32 value rows) walks
+// a range of chunks doing only the state-coupled products.  Each chunk's operands
 // (keys, queries, Linv and P split, the gates, the workgroup's value columns)
 // are copied global -> LDS asynchronously one chunk ahead, into the other half
 // of a double buffer, so the walk waits on memory once per chunk at most.
@@ -635,6 +630,11 @@ struct alignas(16) ScanLds {
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 
+template <int V>
+struct IntC {
+    static constexpr int value = V;
+};
+
 // ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
 // i % 4 of the 8 bytes addressed by lane 4 e + i / 4, for e = 0..3.  With lane
 // j addressing row r0 + j / 4 at column c(j % 4) .. + 3 of a row-major 16-bit
@@ -668,20 +668,54 @@ __device__ inline void scan_store_o(const ScanLds<DK> &sm, int n, int lane, int 
 }
 
 // State-coupled products of one chunk (the products of chunk_state) for wave
-// (g, kh), from stage s of the LDS buffers, in the operand mapping above.  st
-// holds the wave's quarter of the state: st[kt][r] is key 32 (KT/2) + 8 lg +
-// 4 (KT%2) + r of value row irow, KT = 4 kh + kt (dk = 128; dk = 64: 2 kh + kt).
-// The pair (g, 0), (g, 1) exchanges partial K S^T and Q S^T through LDS, with
-// the workgroup's barriers between.  Outputs stay in the staging buffer.
-template <int DK>
-__device__ inline void scan_chunk(ScanLds<DK> &sm, int s, float (&st)[DK / 32][4], int n, int lane, int g,
-                                  int kh) {
+// (g, KH), from LDS stage SG, in the operand mapping above.  st holds the
+// wave's quarter of the state: st[kt][r] is key 32 (KT/2) + 8 lg + 4 (KT%2) + r
+// of value row irow, KT = 4 KH + kt (dk = 128; dk = 64: 2 KH + kt).  The pair
+// (g, 0), (g, 1) exchanges partial K S^T and Q S^T through LDS, with the
+// workgroup's barriers between.  Outputs stay in the staging buffer.
+//
+// Every LDS operand is read in two batches ahead of its use: the key, query,
+// value and gate operands first, then (while the partial products run) the
+// Linv, P and transposed-key operands, so the wave waits on LDS latency about
+// twice per chunk rather than once per operand.  Stage and key half are
+// compile-time, so every LDS address is a per-lane base plus a constant.
+template <int DK, int SG, int KH>
+__device__ __forceinline__ void scan_chunk(ScanLds<DK> &sm, float (&st)[DK / 32][4], int n, int lane, int g) {
     constexpr int KTH = DK / 32;   // 16-key state tiles per key half
     constexpr int KBH = DK / 64;   // 32-key contraction blocks per key half
     const int lr = lane & 15, lg = lane >> 4;
-    const uint8_t *Kc = sm.K[s], *Qc = sm.Q[s], *Mc = sm.M[s];
-    const float *Gc = sm.G[s];
-    float *xch = DK == 128 ? reinterpret_cast<float *>(sm.Q[s]) : sm.Xch;
+    const uint8_t *Kc = sm.K[SG], *Qc = sm.Q[SG], *Mc = sm.M[SG];
+    const float *Gc = sm.G[SG];
+    float *xch = DK == 128 ? reinterpret_cast<float *>(sm.Q[SG]) : sm.Xch;
+
+    // Batch 1: keys and queries over this wave's keys (A operands of K S^T and
+    // Q S^T), the workgroup's value columns (transposed) and the gates.  Lane
+    // (lr, lg) of tile 2p + hh holds tokens t0 + r, t0 = 32p + 8lg + 4hh.
+    bf16x8 ka[4][KBH], qa[4][KBH];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+        const int t = tau(tt, lr);
+#pragma unroll
+        for (int p = 0; p < KBH; ++p) {
+            const int piece = 4 * (KBH * KH + p) + lg;
+            ka[tt][p] = lds16(Kc + kq_off<DK>(t, piece));
+            qa[tt][p] = lds16(Qc + kq_off<DK>(t, piece));
+        }
+    }
+    float4 ga[2][2], be[2][2], ee[2][2];
+    bf16x4 vt[2][2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int t0 = 32 * p + 8 * lg + 4 * hh;
+            vt[p][hh] = read_tr(sm.V[SG] + (t0 + (lr >> 2)) * 64 + 32 * g + 8 * (lr & 3));
+            ga[p][hh] = *reinterpret_cast<const float4 *>(Gc + t0);
+            ee[p][hh] = *reinterpret_cast<const float4 *>(Gc + 64 + t0);
+            be[p][hh] = *reinterpret_cast<const float4 *>(Gc + 128 + t0);
+        }
+    const float glast = Gc[n - 1];
+    __builtin_amdgcn_sched_barrier(0);
 
     // Partial X = K S^T and Y = Q S^T over this wave's keys.
     f32x4 X[4], Y[4];
@@ -697,38 +731,72 @@ __device__ inline void scan_chunk(ScanLds<DK> &sm, int s, float (&st)[DK / 32][4
         for (int tt = 0; tt < 4; ++tt) {
             X[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
             Y[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const int t = tau(tt, lr);
 #pragma unroll
             for (int p = 0; p < KBH; ++p) {
-                const int piece = 4 * (KBH * kh + p) + lg;
-                const bf16x8 ka = lds16(Kc + kq_off<DK>(t, piece));
-                const bf16x8 qa = lds16(Qc + kq_off<DK>(t, piece));
-                X[tt] = mma(ka, sB[p].hi, X[tt]);
-                X[tt] = mma(ka, sB[p].lo, X[tt]);
-                Y[tt] = mma(qa, sB[p].hi, Y[tt]);
-                Y[tt] = mma(qa, sB[p].lo, Y[tt]);
+                X[tt] = mma(ka[tt][p], sB[p].hi, X[tt]);
+                X[tt] = mma(ka[tt][p], sB[p].lo, X[tt]);
+                Y[tt] = mma(qa[tt][p], sB[p].hi, Y[tt]);
+                Y[tt] = mma(qa[tt][p], sB[p].lo, Y[tt]);
             }
         }
     }
-    // Exchange: every wave is done reading Q[s] (the exchange space at dk = 128);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // Batch 2: Linv tiles (tt, p <= tt/2) for D, P tiles of this wave's output
+    // tiles tt = KH + 2hh (p <= hh), and K^T for the state update: tile kt's A
+    // operand is K^T at keys 32 (KT/2) + 8 (lr/4) + 4 (KT%2) + lr%4 (row lr) and
+    // tokens 32p + 8lg + {0..7} (slots), two transposed reads of 4 token rows.
+    Split8 li[6], pm[3];
+    bf16x8 kt_a[KTH][2];
+#pragma unroll
+    for (int tt = 0, u = 0; tt < 4; ++tt) {
+        const int t = tau(tt, lr);
+#pragma unroll
+        for (int p = 0; p <= tt / 2; ++p, ++u) {
+            li[u].hi = lds16(Mc + mat_off(0, t, 4 * p + lg));
+            li[u].lo = lds16(Mc + mat_off(1, t, 4 * p + lg));
+        }
+    }
+#pragma unroll
+    for (int hh = 0, u = 0; hh < 2; ++hh) {
+        const int t = tau(KH + 2 * hh, lr);
+#pragma unroll
+        for (int p = 0; p <= hh; ++p, ++u) {
+            pm[u].hi = lds16(Mc + mat_off(2, t, 4 * p + lg));
+            pm[u].lo = lds16(Mc + mat_off(3, t, 4 * p + lg));
+        }
+    }
+#pragma unroll
+    for (int kt = 0; kt < KTH; ++kt) {
+        const int KTg = KTH * KH + kt;
+        const int piece = 4 * (KTg >> 1) + (lr & 3), h8 = (KTg & 1) << 3;
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const int ta = 32 * p + 8 * lg + (lr >> 2);
+            kt_a[kt][p] = cat4(read_tr(Kc + kq_off<DK>(ta, piece) + h8), read_tr(Kc + kq_off<DK>(ta + 4, piece) + h8));
+        }
+    }
+
+    // Exchange: every wave is done reading Q (the exchange space at dk = 128);
     // each wave posts its partial X, and its partial Y of the tiles its partner
     // finalises into those tiles' output staging slots.
     __syncthreads();
     {
-        float *mine = xch + (2 * g + kh) * 1024 + lane * 4;
+        float *mine = xch + (2 * g + KH) * 1024 + lane * 4;
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt)
             *reinterpret_cast<float4 *>(mine + tt * 256) = make_float4(X[tt][0], X[tt][1], X[tt][2], X[tt][3]);
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-            const int tt = (1 - kh) + 2 * hh, t0 = 32 * (tt >> 1) + 8 * lg + 4 * (tt & 1);
+            constexpr int o = 1 - KH;
+            const int tt = o + 2 * hh, t0 = 32 * hh + 8 * lg + 4 * o;
 #pragma unroll
             for (int r = 0; r < 4; ++r) sm.O[(t0 + r) * kOStride + 16 * g + lr] = Y[tt][r];
         }
     }
     __syncthreads();
     {
-        const float *theirs = xch + (2 * g + (1 - kh)) * 1024 + lane * 4;
+        const float *theirs = xch + (2 * g + (1 - KH)) * 1024 + lane * 4;
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
             const float4 o4 = *reinterpret_cast<const float4 *>(theirs + tt * 256);
@@ -739,42 +807,31 @@ __device__ inline void scan_chunk(ScanLds<DK> &sm, int s, float (&st)[DK / 32][4
         }
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-            const int tt = kh + 2 * hh, t0 = 32 * (tt >> 1) + 8 * lg + 4 * (tt & 1);
+            const int tt = KH + 2 * hh, t0 = 32 * hh + 8 * lg + 4 * KH;
 #pragma unroll
             for (int r = 0; r < 4; ++r) Y[tt][r] += sm.O[(t0 + r) * kOStride + 16 * g + lr];
         }
     }
-    // R = diag(beta) (V - diag(gamma) X): lane (lr, lg) of tile tt = 2p + hh holds
-    // tokens t0 + r, t0 = 32p + 8lg + 4hh; v[t0 + r][16g + lr] by a transposed read.
+    // R = diag(beta) (V - diag(gamma) X).
     Split8 rB[2];
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
         float x[8];
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            const int tt = 2 * p + hh, t0 = 32 * p + 8 * lg + 4 * hh;
-            const bf16x4 vt = read_tr(sm.V[s] + (t0 + (lr >> 2)) * 64 + 32 * g + 8 * (lr & 3));
-            const float4 ga = *reinterpret_cast<const float4 *>(Gc + t0);
-            const float4 be = *reinterpret_cast<const float4 *>(Gc + 128 + t0);
+        for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                x[4 * hh + r] = (&be.x)[r] * (static_cast<float>(vt[r]) - (&ga.x)[r] * X[tt][r]);
-        }
+                x[4 * hh + r] = (&be[p][hh].x)[r] *
+                                (static_cast<float>(vt[p][hh][r]) - (&ga[p][hh].x)[r] * X[2 * p + hh][r]);
         rB[p] = split8(x);
     }
-    // D = Linv R (both waves of the pair; Linv is lower triangular: p <= tt / 2).
+    // D = Linv R (Linv is lower triangular: p <= tt / 2).
     f32x4 D[4];
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
+    for (int tt = 0, u = 0; tt < 4; ++tt) {
         D[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int t = tau(tt, lr);
 #pragma unroll
-        for (int p = 0; p <= tt / 2; ++p) {
-            Split8 a;
-            a.hi = lds16(Mc + mat_off(0, t, 4 * p + lg));
-            a.lo = lds16(Mc + mat_off(1, t, 4 * p + lg));
-            D[tt] = mma3(a, rB[p], D[tt]);
-        }
+        for (int p = 0; p <= tt / 2; ++p, ++u) D[tt] = mma3(li[u], rB[p], D[tt]);
     }
     // D split twice: as is (for P D) and scaled by e (for the state update).
     Split8 dB[2], eB[2];
@@ -782,64 +839,48 @@ __device__ inline void scan_chunk(ScanLds<DK> &sm, int s, float (&st)[DK / 32][4
     for (int p = 0; p < 2; ++p) {
         float x[8], y[8];
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            const int tt = 2 * p + hh;
-            const float4 ee = *reinterpret_cast<const float4 *>(Gc + 64 + 32 * p + 8 * lg + 4 * hh);
+        for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                x[4 * hh + r] = D[tt][r];
-                y[4 * hh + r] = (&ee.x)[r] * D[tt][r];
+                x[4 * hh + r] = D[2 * p + hh][r];
+                y[4 * hh + r] = (&ee[p][hh].x)[r] * D[2 * p + hh][r];
             }
-        }
         dB[p] = split8(x);
         eB[p] = split8(y);
     }
-    // O = diag(gamma) Y + P D for this wave's tiles kh and kh + 2, into staging.
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-        const int tt = kh + 2 * hh;
-        const int t = tau(tt, lr), t0 = 32 * (tt >> 1) + 8 * lg + 4 * (tt & 1);
-        const float4 ga = *reinterpret_cast<const float4 *>(Gc + t0);
-        f32x4 Ot = Y[tt];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Ot[r] *= (&ga.x)[r];
-#pragma unroll
-        for (int p = 0; p <= hh; ++p) {   // p <= tt / 2 = hh
-            Split8 a;
-            a.hi = lds16(Mc + mat_off(2, t, 4 * p + lg));
-            a.lo = lds16(Mc + mat_off(3, t, 4 * p + lg));
-            Ot = mma3(a, dB[p], Ot);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sm.O[(t0 + r) * kOStride + 16 * g + lr] = Ot[r];
-    }
-    // S <- gamma_last S + K^T diag(e) D over this wave's keys.  Tile KT's A
-    // operand is K^T at keys 32 (KT/2) + 8 (lr/4) + 4 (KT%2) + lr%4 (row lr) and
-    // tokens 32p + 8lg + {0..7} (slots): two transposed reads of 4 token rows.
-    const float glast = Gc[n - 1];
+    // S <- gamma_last S + K^T diag(e) D over this wave's keys.
 #pragma unroll
     for (int kt = 0; kt < KTH; ++kt) {
-        const int KTg = KTH * kh + kt;
         f32x4 U = {0.f, 0.f, 0.f, 0.f};
-        const int piece = 4 * (KTg >> 1) + (lr & 3), h8 = (KTg & 1) << 3;
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-            const int ta = 32 * p + 8 * lg + (lr >> 2);
-            const bf16x8 ka = cat4(read_tr(Kc + kq_off<DK>(ta, piece) + h8),
-                                   read_tr(Kc + kq_off<DK>(ta + 4, piece) + h8));
-            U = mma(ka, eB[p].hi, U);
-            U = mma(ka, eB[p].lo, U);
+            U = mma(kt_a[kt][p], eB[p].hi, U);
+            U = mma(kt_a[kt][p], eB[p].lo, U);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) st[kt][r] = glast * st[kt][r] + U[r];
     }
+    // O = diag(gamma) Y + P D for this wave's tiles KH and KH + 2, into staging.
+#pragma unroll
+    for (int hh = 0, u = 0; hh < 2; ++hh) {
+        const int tt = KH + 2 * hh, t0 = 32 * hh + 8 * lg + 4 * KH;
+        f32x4 Ot = Y[tt];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Ot[r] *= (&ga[hh][KH].x)[r];
+#pragma unroll
+        for (int p = 0; p <= hh; ++p, ++u) Ot = mma3(pm[u], dB[p], Ot);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sm.O[(t0 + r) * kOStride + 16 * g + lr] = Ot[r];
+    }
 }
 
 template <int DK, int DV>
-__global__ __launch_bounds__(256) void prefill_scan_kernel(
-    float *__restrict__ S, const __hip_bfloat16 *__restrict__ q, const __hip_bfloat16 *__restrict__ k,
-    const __hip_bfloat16 *__restrict__ v, int L, int H, int nchunks, const float *__restrict__ ws,
-    float *__restrict__ o) {
+__device__ __forceinline__ void scan_role(ScanLds<DK> &sm, int wg, int nscan, float *__restrict__ S,
+                                          const __hip_bfloat16 *__restrict__ q,
+                                          const __hip_bfloat16 *__restrict__ k,
+                                          const __hip_bfloat16 *__restrict__ v, int L, int H, int nchunks,
+                                          int cbeg, int cend, const uint8_t *__restrict__ ws,
+                                          float *__restrict__ o) {
     constexpr int RS = 32;                  // value rows per workgroup
     constexpr int NW = 4;                   // waves: 2 row groups x 2 key halves
     constexpr int SLICES = DV / RS;
@@ -847,15 +888,13 @@ __global__ __launch_bounds__(256) void prefill_scan_kernel(
     constexpr int NKQ = C * DK * 2 / 1024;  // 1 KiB blocks of a key or query chunk
     static_assert(SLICES * RS == DV && NKQ % NW == 0, "tiling");
 
-    __shared__ ScanLds<DK> sm;
-
     // Workgroup i runs on XCD i % 8.  The SLICES workgroups of one head read the
     // same keys, queries and chunk matrices, so they are placed on one XCD, where
     // its L2 serves the repeats: within each group of 8 SLICES workgroups, XCD x
     // takes head 8 g + x, slice = position / 8.  A ragged last group maps linearly.
-    const int wg = blockIdx.x, grp = 8 * SLICES;
+    const int grp = 8 * SLICES;
     int bh, slice;
-    if (wg < int(gridDim.x) / grp * grp) {
+    if (wg < nscan / grp * grp) {
         const int g0 = wg / grp, r = wg - g0 * grp;
         bh = 8 * g0 + (r & 7);
         slice = r >> 3;
@@ -887,7 +926,7 @@ __global__ __launch_bounds__(256) void prefill_scan_kernel(
     const __hip_bfloat16 *kb = k + (size_t(b) * L * H + h) * DK;   // token row t at + t H DK
     const __hip_bfloat16 *qb = q + (size_t(b) * L * H + h) * DK;
     const __hip_bfloat16 *vb = v + (size_t(b) * L * H + h) * DV + slice * RS;
-    const uint8_t *wsh = reinterpret_cast<const uint8_t *>(ws) + size_t(bh) * nchunks * kPrepBytes;
+    const uint8_t *wsh = ws + size_t(bh) * nchunks * kPrepBytes;
     const size_t kstride = size_t(H) * DK, vstride = size_t(H) * DV;
 
     // Copy chunk cn's operands into stage cn & 1.  Wave w takes the 1 KiB blocks
@@ -912,7 +951,7 @@ __global__ __launch_bounds__(256) void prefill_scan_kernel(
     const uint32_t vo_v = uint32_t(lane >> 2) * vstride_b + 16u * uint32_t(lane & 3);
     const uint32_t vo_g = 16u * uint32_t(min(lane, 3 * C / 4 - 1));
     auto issue = [&](int cn) {
-        const int s = cn & 1, c0 = cn * C;
+        const int s = (cn - cbeg) & 1, c0 = cn * C;
         const uint8_t *rec = wsh + size_t(cn) * kPrepBytes;
         const uint32_t lk = lds_addr(sm.K[s]), lq = lds_addr(sm.Q[s]), lm = lds_addr(sm.M[s]),
                        lv = lds_addr(sm.V[s]);
@@ -951,21 +990,31 @@ __global__ __launch_bounds__(256) void prefill_scan_kernel(
     // c + 1, so the wait at the top of each chunk finds the stores long done.
     float *ob = o + (size_t(b) * L * H + h) * DV + slice * RS;
     const size_t ostride = size_t(H) * DV;
-    issue(0);
-    for (int c = 0; c < nchunks; ++c) {
+    // One step per chunk; the loop is unrolled over the two LDS stages so that
+    // stage and key half are compile-time inside scan_chunk.
+    auto step = [&](int c, auto stage) __attribute__((always_inline)) {
+        constexpr int SG = decltype(stage)::value;
         const int c0 = c * C, n = min(C, L - c0);
         // This chunk's copies (issued one chunk ago) have landed, for every wave,
         // and every wave is done with the buffers the next copies overwrite.
         __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) expcnt(7) lgkmcnt(0)
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        if (c > 0) scan_store_o<DK>(sm, C, lane, g, kh, ob + size_t(c0 - C) * ostride, ostride);
-        if (c + 1 < nchunks) issue(c + 1);
+        if (c > cbeg) scan_store_o<DK>(sm, C, lane, g, kh, ob + size_t(c0 - C) * ostride, ostride);
+        if (c + 1 < cend) issue(c + 1);
         asm volatile("" ::: "memory");
-        scan_chunk<DK>(sm, c & 1, st, n, lane, g, kh);
+        if (kh)
+            scan_chunk<DK, SG, 1>(sm, st, n, lane, g);
+        else
+            scan_chunk<DK, SG, 0>(sm, st, n, lane, g);
+    };
+    issue(cbeg);
+    for (int c = cbeg; c < cend; c += 2) {
+        step(c, IntC<0>{});
+        if (c + 1 < cend) step(c + 1, IntC<1>{});
     }
     asm volatile("" ::: "memory");
-    scan_store_o<DK>(sm, L - (nchunks - 1) * C, lane, g, kh, ob + size_t(nchunks - 1) * C * ostride, ostride);
+    scan_store_o<DK>(sm, min(C, L - (cend - 1) * C), lane, g, kh, ob + size_t(cend - 1) * C * ostride, ostride);
 
 #pragma unroll
     for (int kt = 0; kt < KTH; ++kt) {
@@ -973,6 +1022,57 @@ __global__ __launch_bounds__(256) void prefill_scan_kernel(
         *reinterpret_cast<float4 *>(Srow + 32 * (KT >> 1) + 8 * lg + 4 * (KT & 1)) =
             make_float4(st[kt][0], st[kt][1], st[kt][2], st[kt][3]);
     }
+}
+
+template <int DK>
+union FusedLds {
+    PrepSmem<DK> prep;
+    ScanLds<DK> scan;
+};
+
+// Prep records of chunks [pbeg, pend) for every (instance, head): unit u =
+// chunk-relative index * heads + head, workgroup u % nprep.
+template <int DK>
+__device__ __forceinline__ void prep_role(PrepSmem<DK> &sm, int wg, int nprep, const __hip_bfloat16 *__restrict__ q,
+                                          const __hip_bfloat16 *__restrict__ k, const float *__restrict__ g,
+                                          const float *__restrict__ beta, int L, int H, int heads, int nchunks,
+                                          int pbeg, int pend, uint8_t *__restrict__ ws) {
+    const int units = heads * (pend - pbeg);
+    for (int u = wg; u < units; u += nprep) {
+        const int c = pbeg + u / heads, bh = u % heads;
+        __syncthreads();  // the previous unit's LDS reads are done
+        prep_unit<DK>(sm, q, k, g, beta, L, H, nchunks, ws, bh, c);
+    }
+}
+
+// One stage of the pipelined two-phase schedule: workgroups [0, nprep) build
+// the prep records of chunks [pbeg, pend) while workgroups [nprep, nprep +
+// nscan) scan chunks [cbeg, cend), whose records an earlier launch built.  The
+// two roles share nothing, so no workgroup waits on another; the prep runs on
+// the compute units the scan leaves idle.
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void prefill_stage_kernel(
+    float *__restrict__ S, const __hip_bfloat16 *__restrict__ q, const __hip_bfloat16 *__restrict__ k,
+    const __hip_bfloat16 *__restrict__ v, const float *__restrict__ g, const float *__restrict__ beta, int L,
+    int H, int heads, int nchunks, int cbeg, int cend, int pbeg, int pend, int nprep, int nscan,
+    uint8_t *__restrict__ ws, float *__restrict__ o) {
+    __shared__ FusedLds<DK> sm;
+    const int wg = blockIdx.x;
+    if (wg < nprep)
+        prep_role<DK>(sm.prep, wg, nprep, q, k, g, beta, L, H, heads, nchunks, pbeg, pend, ws);
+    else
+        scan_role<DK, DV>(sm.scan, wg - nprep, nscan, S, q, k, v, L, H, nchunks, cbeg, cend, ws, o);
+}
+
+// Prep records of chunks [pbeg, pend) on the whole chip (two workgroups a
+// compute unit: this kernel needs only the prep's LDS).
+template <int DK>
+__global__ __launch_bounds__(256) void prefill_prep_kernel(
+    const __hip_bfloat16 *__restrict__ q, const __hip_bfloat16 *__restrict__ k, const float *__restrict__ g,
+    const float *__restrict__ beta, int L, int H, int heads, int nchunks, int pbeg, int pend,
+    uint8_t *__restrict__ ws) {
+    __shared__ PrepSmem<DK> sm;
+    prep_role<DK>(sm, blockIdx.x, gridDim.x, q, k, g, beta, L, H, heads, nchunks, pbeg, pend, ws);
 }
 
 template <int DK, int DV>
@@ -985,13 +1085,44 @@ hipError_t launch_dk_dv(float *S, const void *q, const void *k, const void *v, c
     const long heads = long(s.B) * s.H;
     const int nchunks = (L + C - 1) / C;
     if (heads < kFewHeads && ws != nullptr && ws_bytes >= size_t(heads) * nchunks * kPrepBytes) {
-        hipLaunchKernelGGL((prefill_prep_kernel<DK>), dim3(unsigned(heads * nchunks)), dim3(256), 0, st,
-                           qq, kk, g, beta, L, s.H, nchunks, static_cast<float *>(ws));
+        uint8_t *wsb = static_cast<uint8_t *>(ws);
+        const int nscan = int(heads) * (DV / 32);
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            cus = 0;
+        // Prep workgroups beside the scan: the compute units it leaves idle, in
+        // multiples of 8 so scan workgroup i stays on XCD i % 8.
+        const int nside = (cus - nscan) / 8 * 8;
+        // Chunk segments: the first is prepped alone, each later one while the
+        // scan walks the one before.  A side prep on the idle compute units
+        // keeps pace with the scan chunk for chunk, so the segments are equal.
+        // Short prompts, or a scan that leaves too few units idle, use one
+        // segment (prep, then scan).
+        constexpr int kSeg = 3;
+        int bnd[kSeg + 2], nseg = 1;
+        bnd[0] = 0;
+        bnd[1] = nchunks;
+        if (nchunks >= 4 * kSeg && nside >= 8 && 2 * nside >= nscan) {
+            nseg = kSeg;
+            for (int j = 1; j <= kSeg; ++j) bnd[j] = nchunks * j / kSeg;
+        }
+        bnd[nseg + 1] = nchunks;
+        const int units0 = int(heads) * bnd[1];
+        hipLaunchKernelGGL((prefill_prep_kernel<DK>), dim3(unsigned(units0)), dim3(256), 0, st, qq, kk, g, beta, L,
+                           s.H, int(heads), nchunks, 0, bnd[1], wsb);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((prefill_scan_kernel<DK, DV>), dim3(unsigned(heads * (DV / 32))), dim3(256), 0, st,
-                           S, qq, kk, vv, L, s.H, nchunks, static_cast<const float *>(ws), o);
-        return hipGetLastError();
+        for (int j = 0; j < nseg; ++j) {
+            const int pbeg = bnd[j + 1], pend = j + 1 < nseg ? bnd[j + 2] : pbeg;
+            const int nprep = pend > pbeg ? std::min(nside, int(heads) * (pend - pbeg) + 7) / 8 * 8 : 0;
+            hipLaunchKernelGGL((prefill_stage_kernel<DK, DV>), dim3(unsigned(nprep + nscan)), dim3(256), 0, st, S,
+                               qq, kk, vv, g, beta, L, s.H, int(heads), nchunks, bnd[j], bnd[j + 1], pbeg, pend,
+                               nprep, nscan, wsb, o);
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
     }
     // One pass: one workgroup per head.
     hipLaunchKernelGGL((prefill_kernel<DK, DV, DV / 16>), dim3(unsigned(heads)), dim3(4 * DV), 0, st,

@@ -34,20 +34,11 @@ __device__ inline float comp(const float4 &v, int c) {
     return c == 0 ? v.x : c == 1 ? v.y : c == 2 ? v.z : v.w;
 }
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-
-// Split eight fp32 values (two float4) into high and low bf16 parts:
-// x = hi + lo + r with |r| <= 2^-17 |x|; products with exact bf16 operands are
-// exact in the fp32 MFMA accumulator.
+// Split eight fp32 values (two float4) into high and low bf16 parts; products
+// with exact bf16 operands are exact in the fp32 MFMA accumulator.
 __device__ inline void split_bf16(const float4 &a, const float4 &b, bf16x8 &hi, bf16x8 &lo) {
     const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const __bf16 hh = static_cast<__bf16>(x[e]);
-        hi[e] = hh;
-        lo[e] = static_cast<__bf16>(x[e] - static_cast<float>(hh));
-    }
+    split8_bf16(x, hi, lo);
 }
 
 // bf16 X rows are 2 dk bytes, unpadded, with their 16-byte pieces in swizzled

@@ -184,7 +184,7 @@ def test_prefill_48_layers_32k_then_256_rounds(G):
 @pytest.mark.parametrize("schedule", ["two_pass", "one_pass"])
 @pytest.mark.parametrize("dk,dv,L", [(128, 128, 300), (64, 128, 129), (128, 64, 64)])
 def test_prefill_both_schedules(G, schedule, dk, dv, L):
-    """Few heads run two passes (parallel chunk prep into the workspace, then the
+    """Few heads run two phases (parallel chunk prep into the workspace, and the
     scan) when given the workspace, and one pass without it; both reach the
     sequential oracle."""
     B, H = 1, 4
