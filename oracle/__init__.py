@@ -15,3 +15,4 @@ from .gdn_oracle import (  # noqa: F401
     prefill_seq,
     prefill_chunked,
 )
+from . import accept_oracle  # noqa: F401,E402  (acceptance and rewind, numpy fp64)

@@ -50,6 +50,24 @@ def test_prefill_shapes_and_tails(G, dk, dv, L):
     assert rel_err_state(S, ref_S) <= STATE_TOL
 
 
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (128, 64)])
+def test_prefill_segmented_schedule_ragged(G, dk, dv):
+    """Few heads and enough chunks (17, the last partial) that the two-phase
+    schedule cuts the prompt into segments, each segment's prep running beside
+    the previous segment's scan: every output and the final state against the
+    sequential oracle."""
+    B, H, L = 1, 3, 16 * 64 + 37
+    print_case(test="prefill_segmented", B=B, H=H, dk=dk, dv=dv, L=L, seed=57)
+    x = make_inputs(B, H, dk, dv, L, seed=57, device=DEV)
+    xc = x.to("cpu")
+    o, S = run_prefill(G, x)
+    ref_o, ref_S = oracle.prefill_seq(xc.S0, xc.q, xc.k, xc.v, xc.g, xc.beta)
+    assert not torch.isnan(o).any()
+    eo, es = rel_err_outputs(o, ref_o), rel_err_state(S, ref_S)
+    print(f"prefill_segmented: out err {eo:.3e} state err {es:.3e}", flush=True)
+    assert eo <= OUT_TOL and es <= STATE_TOL
+
+
 def test_prefill_4096_tokens_32_heads(G):
     """One layer, 32 heads, d = 128, 4,096 tokens, chunk 64: every output and the
     final state against the sequential oracle."""
