@@ -219,6 +219,102 @@ int gdn_prefill_chunked(float *S, const void *q, const void *k, const void *v,
                         gdn_in_dtype in_dt, const gdn_shape *shp, float *o, void *ws,
                         size_t ws_bytes, void *hip_stream);
 
+/* ---------------------------------------------------------------------------
+ * Acceptance and rewind, on the device.
+ *
+ * Source: the audited-numbers page ("Qwen 3.8 27B mac m5: 200 tok/s, audited"),
+ * section "How does DSpark speculative decoding create more than one token per
+ * read?": acceptance is exact speculative sampling -- greedy keeps a drafted
+ * token only where it equals the target model's token, sampled keeps it with
+ * probability min(1, p/q) -- and the pass emits a correction token at the first
+ * rejection or a bonus token when every draft was kept; rewind then brings the
+ * key-value cache, the short filter history and the recurrent state in line with
+ * the kept tokens.  The README page ("How it works") keeps positions, accepted
+ * tokens and commit/rollback on the GPU: here n_out feeds gdn_commit (or
+ * gdn_commit_verify) directly, which rewinds the recurrent state and advances the
+ * position (the key-value length) by n; gdn_history_rewind does the filter
+ * history.  Nothing is read back to the host.
+ *
+ * A verify block's T rows are [anchor, d_1, .., d_{T-1}]: the last confirmed
+ * token and T - 1 drafted tokens.  Target row t's logits give the distribution of
+ * the token after row t; drafter row j (0 .. T-2) is the distribution d_{j+1} was
+ * drawn from.  n_out[b] = 1 + (drafts kept) rows are confirmed, 1..T; the
+ * emitted token (next_token[b]) is the next block's anchor.
+ * ------------------------------------------------------------------------- */
+#define GDN_HISTORY_MAX 16
+
+/* B sequences, T rows per block (1..GDN_T_MAX), V vocabulary entries (1..2^26). */
+typedef struct {
+    int32_t B, T, V;
+} gdn_accept_shape;
+
+/* Workspace bytes of gdn_accept_greedy (sampled = 0) or gdn_accept_sampled
+ * (sampled = 1); 0 for an invalid shape. */
+size_t gdn_accept_workspace_bytes(const gdn_accept_shape *shp, int32_t sampled);
+
+/*
+ * Greedy acceptance.  Draft d_{j+1} is kept while it equals the argmax of target
+ * row j (the lowest index among equal logits); n_out[b] = 1 + kept drafts and
+ * next_token[b] = the argmax of target row n_out[b] - 1 (the correction, or the
+ * bonus when all T - 1 drafts were kept).
+ *
+ *   target_logits  [B][T][V], dtype dt (bf16 or fp32), finite values.
+ *   draft_tokens   int32 [B][T-1] (may be NULL when T = 1); a token outside
+ *                  [0, V) is never kept.
+ *   n_out, next_token   int32 [B], written.
+ *   ws             device workspace of gdn_accept_workspace_bytes(shp, 0) bytes,
+ *                  16-byte aligned; contents are scratch.
+ * All pointers are device memory owned by the caller.  Returns GDN_OK, or a
+ * negative status before anything is launched: GDN_EDIM (B < 1 or V out of
+ * range), GDN_ERANGE (T out of range), GDN_EWS, GDN_EINVAL (null or misaligned
+ * pointer, unknown dtype), GDN_EHIP.
+ */
+int gdn_accept_greedy(const void *target_logits, gdn_in_dtype dt, const int32_t *draft_tokens,
+                      const gdn_accept_shape *shp, int32_t *n_out, int32_t *next_token, void *ws,
+                      size_t ws_bytes, void *hip_stream);
+
+/*
+ * Sampled acceptance (exact speculative sampling).  With p = softmax(target row /
+ * temperature) and q = softmax(drafter row / temperature), draft d_{j+1} is kept
+ * while u_accept[b][j] * q(d) < p(d) (the event u < min(1, p/q)).  At the first
+ * rejection, at row m, next_token[b] is drawn from max(0, p - q) normalised;
+ * when every draft was kept, from p of target row T - 1.  A draw from weights w
+ * with uniform u is the smallest x with w_0 + .. + w_x > u (w_0 + .. + w_{V-1});
+ * it never returns a zero-weight entry (if the weights underflow to zero in
+ * fp32, the row's argmax is returned).
+ *
+ *   target_logits  [B][T][V]; draft_logits [B][T-1][V] (may be NULL when T = 1);
+ *                  both dtype dt, finite.
+ *   draft_tokens   int32 [B][T-1]; a token outside [0, V) is rejected.
+ *   u_accept       fp32 [B][T-1] in [0, 1); u_sample fp32 [B] in [0, 1): the
+ *                  random numbers, drawn by the caller.
+ *   temperature    > 0, finite.
+ *   n_out, next_token, ws   as for the greedy call (ws of
+ *                  gdn_accept_workspace_bytes(shp, 1) bytes).
+ * Arithmetic is fp32; decisions within fp32 rounding of their threshold may
+ * differ from an exact computation.  Errors as for the greedy call, plus
+ * GDN_ERANGE for a temperature that is not positive and finite.
+ */
+int gdn_accept_sampled(const void *target_logits, const void *draft_logits, gdn_in_dtype dt,
+                       const int32_t *draft_tokens, const float *u_accept, const float *u_sample,
+                       float temperature, const gdn_accept_shape *shp, int32_t *n_out, int32_t *next_token,
+                       void *ws, size_t ws_bytes, void *hip_stream);
+
+/*
+ * Rewind of the filter history (the short causal filter before the mixer keeps
+ * its last W inputs).  In place: history[b] becomes the last W rows of
+ * [history[b]; rows[b][0 .. n[b]-1]], the history as if only the n[b] confirmed
+ * rows of the block had been fed.
+ *
+ *   history  [B][W][C], dtype dt, updated in place;  rows [B][T][C], dtype dt:
+ *            the block's filter inputs;  n  int32 [B] on the device (n_out of an
+ *            acceptance call); an n outside [0, T] leaves that history unchanged.
+ *   W in 1..GDN_HISTORY_MAX, T in 1..GDN_T_MAX, C >= 1.
+ * Returns GDN_OK, GDN_EDIM, GDN_ERANGE, GDN_EINVAL or GDN_EHIP.
+ */
+int gdn_history_rewind(void *history, const void *rows, const int32_t *n, int32_t B, int32_t W, int32_t T,
+                       int32_t C, gdn_in_dtype dt, void *hip_stream);
+
 /* Static description of a gdn_status value; never NULL. */
 const char *gdn_strerror(int status);
 

@@ -1,0 +1,442 @@
+// accept.hip -- acceptance of a verify block and rewind of the filter history,
+// on the device.
+//
+// Acceptance is exact speculative sampling (the audited-numbers page, "How does
+// DSpark speculative decoding create more than one token per read?").  Rows of
+// the block are [anchor, d_1 .. d_{T-1}]; target row t's logits give the
+// distribution of the token after row t, drafter row j the distribution d_{j+1}
+// was drawn from.  Greedy keeps d_{j+1} while it equals target row j's argmax
+// (lowest index among equals); sampled keeps it while u_j q(d) < p(d), with
+// p = softmax(target / tau) and q = softmax(drafter / tau).  n = 1 + (kept
+// drafts) rows are committed; the emitted token is the argmax of the first
+// unmatched row (greedy), or a draw from max(0, p - q) at the first rejection /
+// from p of the last row when every draft was kept (sampled).  A draw from
+// weights w with uniform u is the smallest x with w_0 + .. + w_x > u sum(w).
+//
+// The work is a few passes over vocabulary rows, bound by memory traffic and
+// launch latency.  Rows are cut into slices of kSlice entries, one workgroup
+// each:
+//   stats  (B x rows x slices): per slice, the argmax of the raw logits and, for
+//          sampled mode, max and sum of exp of logits / tau;
+//   decide (B, one wave): combine the slices of each row, walk the drafts in
+//          order, write n (and, greedy, the emitted token);
+//   mass   (B x slices, sampled): per slice, the mass of the weights the
+//          emitted token is drawn from;
+//   pick   (B, sampled): find the slice, then the entry, where the cumulative
+//          weight passes u times the total.
+#include <climits>
+
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+constexpr int kSlice = 4096;              // vocabulary entries per workgroup
+constexpr int kThreads = 256;
+constexpr int kPer = kSlice / kThreads;   // entries per thread
+
+// Per-slice statistics of one row: max of x = logit / tau, sum of exp(x - max),
+// the largest raw logit and its (lowest) index.
+struct Part {
+    float m, s, bv;
+    int bi;
+};
+
+// What decide hands to mass and pick for one sequence.
+struct Pick {
+    int row;        // target (and drafter) row the token is drawn at
+    int residual;   // 1: weights max(0, p - q); 0: weights p (bonus)
+    float mt, st;   // target row: max and sum of exp
+    float md, sd;   // drafter row (residual only)
+    int amax;       // target row's argmax: the answer when the weights sum to 0
+    int pad;
+};
+
+template <typename TIn>
+__device__ inline float ld(const TIn *p, size_t i);
+template <>
+__device__ inline float ld<float>(const float *p, size_t i) {
+    return p[i];
+}
+template <>
+__device__ inline float ld<__hip_bfloat16>(const __hip_bfloat16 *p, size_t i) {
+    return bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(p)[i]);
+}
+
+// (max, sum of exp) pairs: merge b into a.
+__device__ inline void lse_merge(float &m, float &s, float m2, float s2) {
+    if (m2 > m) {
+        const float t = m;
+        m = m2;
+        m2 = t;
+        const float u = s;
+        s = s2;
+        s2 = u;
+    }
+    if (m2 != -INFINITY) s += s2 * __expf(m2 - m);
+}
+
+// Argmax pairs: larger value, then lower index.
+__device__ inline void amax_merge(float &v, int &i, float v2, int i2) {
+    if (v2 > v || (v2 == v && i2 < i)) {
+        v = v2;
+        i = i2;
+    }
+}
+
+template <typename TIn>
+__device__ inline const TIn *row_ptr(const TIn *tgt, const TIn *drf, int b, int r, int T, int V) {
+    return r < T ? tgt + (size_t(b) * T + r) * V : drf + (size_t(b) * (T - 1) + (r - T)) * V;
+}
+
+template <typename TIn, bool SAMPLED>
+__global__ __launch_bounds__(kThreads) void accept_stats_kernel(const TIn *__restrict__ tgt,
+                                                                const TIn *__restrict__ drf, int T, int V,
+                                                                int ns, float inv_tau, Part *__restrict__ parts) {
+    const int s = blockIdx.x, r = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+    const TIn *row = row_ptr(tgt, drf, b, r, T, V);
+    const int lo = s * kSlice, hi = min(V, lo + kSlice);
+    float x[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int i = lo + tid + k * kThreads;
+        x[k] = i < hi ? ld(row, i) : -INFINITY;
+    }
+    float bv = -INFINITY;
+    int bi = INT_MAX;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int i = lo + tid + k * kThreads;
+        if (i < hi && (x[k] > bv || bi == INT_MAX)) {   // k ascending: strict > keeps the lowest index
+            bv = x[k];
+            bi = i;
+        }
+    }
+    float m = -INFINITY, sum = 0.f;
+    if constexpr (SAMPLED) {
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) m = fmaxf(m, x[k] * inv_tau);
+        if (m != -INFINITY) {
+#pragma unroll
+            for (int k = 0; k < kPer; ++k) sum += __expf(x[k] * inv_tau - m);
+        }
+    }
+    // Wave reduction, then across the four waves through LDS.
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        amax_merge(bv, bi, __shfl_xor(bv, off, 64), __shfl_xor(bi, off, 64));
+        if constexpr (SAMPLED) lse_merge(m, sum, __shfl_xor(m, off, 64), __shfl_xor(sum, off, 64));
+    }
+    __shared__ Part wp[kThreads / 64];
+    const int w = tid >> 6;
+    if ((tid & 63) == 0) wp[w] = Part{m, sum, bv, bi};
+    __syncthreads();
+    if (tid == 0) {
+        Part p = wp[0];
+#pragma unroll
+        for (int j = 1; j < kThreads / 64; ++j) {
+            amax_merge(p.bv, p.bi, wp[j].bv, wp[j].bi);
+            if constexpr (SAMPLED) lse_merge(p.m, p.s, wp[j].m, wp[j].s);
+        }
+        parts[(size_t(b) * gridDim.y + r) * ns + s] = p;
+    }
+}
+
+// One wave per sequence: combine the slices of every row, then walk the drafts.
+template <typename TIn, bool SAMPLED>
+__global__ __launch_bounds__(64) void accept_decide_kernel(
+    const TIn *__restrict__ tgt, const TIn *__restrict__ drf, const int32_t *__restrict__ drafts,
+    const float *__restrict__ u_acc, int T, int V, int ns, float inv_tau, const Part *__restrict__ parts,
+    Pick *__restrict__ pick, int32_t *__restrict__ n_out, int32_t *__restrict__ next) {
+    const int b = blockIdx.x, lane = threadIdx.x;
+    const int rows = SAMPLED ? 2 * T - 1 : T;
+    __shared__ float M[2 * GDN_T_MAX], S[2 * GDN_T_MAX];
+    __shared__ int AM[2 * GDN_T_MAX];
+    for (int r = 0; r < rows; ++r) {
+        const Part *pr = parts + (size_t(b) * rows + r) * ns;
+        float m = -INFINITY, s = 0.f, bv = -INFINITY;
+        int bi = INT_MAX;
+        for (int j = lane; j < ns; j += 64) {
+            const Part p = pr[j];
+            amax_merge(bv, bi, p.bv, p.bi);
+            if constexpr (SAMPLED) lse_merge(m, s, p.m, p.s);
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            amax_merge(bv, bi, __shfl_xor(bv, off, 64), __shfl_xor(bi, off, 64));
+            if constexpr (SAMPLED) lse_merge(m, s, __shfl_xor(m, off, 64), __shfl_xor(s, off, 64));
+        }
+        if (lane == 0) {
+            M[r] = m;
+            S[r] = s;
+            AM[r] = bi;
+        }
+    }
+    __syncthreads();
+    if (lane != 0) return;
+    const int32_t *db = T > 1 ? drafts + size_t(b) * (T - 1) : nullptr;
+    int m = 0;
+    if constexpr (!SAMPLED) {
+        while (m < T - 1 && db[m] == AM[m]) ++m;
+        next[b] = AM[m];
+    } else {
+        const float *ub = T > 1 ? u_acc + size_t(b) * (T - 1) : nullptr;
+        while (m < T - 1) {
+            const int d = db[m];
+            if (d < 0 || d >= V) break;   // an out-of-range draft is rejected
+            const float p = __expf(ld(tgt, (size_t(b) * T + m) * V + d) * inv_tau - M[m]) / S[m];
+            const float q = __expf(ld(drf, (size_t(b) * (T - 1) + m) * V + d) * inv_tau - M[T + m]) / S[T + m];
+            if (!(ub[m] * q < p)) break;
+            ++m;
+        }
+        Pick pk;
+        pk.row = m;
+        pk.residual = m < T - 1;
+        pk.mt = M[m];
+        pk.st = S[m];
+        pk.md = pk.residual ? M[T + m] : 0.f;
+        pk.sd = pk.residual ? S[T + m] : 1.f;
+        pk.amax = AM[m];
+        pk.pad = 0;
+        pick[b] = pk;
+    }
+    n_out[b] = m + 1;
+}
+
+// Weight of vocabulary entry i in the draw: p(i), or max(0, p(i) - q(i)).
+template <typename TIn>
+__device__ inline float draw_weight(const TIn *trow, const TIn *drow, const Pick &pk, float inv_tau, int i) {
+    const float p = __expf(ld(trow, i) * inv_tau - pk.mt) / pk.st;
+    if (!pk.residual) return p;
+    const float q = __expf(ld(drow, i) * inv_tau - pk.md) / pk.sd;
+    return fmaxf(p - q, 0.f);
+}
+
+template <typename TIn>
+__global__ __launch_bounds__(kThreads) void accept_mass_kernel(const TIn *__restrict__ tgt,
+                                                               const TIn *__restrict__ drf, int T, int V, int ns,
+                                                               float inv_tau, const Pick *__restrict__ pick,
+                                                               float *__restrict__ mass) {
+    const int s = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const Pick pk = pick[b];
+    const TIn *trow = tgt + (size_t(b) * T + pk.row) * V;
+    const TIn *drow = pk.residual ? drf + (size_t(b) * (T - 1) + pk.row) * V : nullptr;
+    const int lo = s * kSlice, hi = min(V, lo + kSlice);
+    float acc = 0.f;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int i = lo + tid + k * kThreads;
+        if (i < hi) acc += draw_weight(trow, drow, pk, inv_tau, i);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    __shared__ float ws[kThreads / 64];
+    if ((tid & 63) == 0) ws[tid >> 6] = acc;
+    __syncthreads();
+    if (tid == 0) mass[size_t(b) * ns + s] = (ws[0] + ws[1]) + (ws[2] + ws[3]);
+}
+
+template <typename TIn>
+__global__ __launch_bounds__(kThreads) void accept_pick_kernel(const TIn *__restrict__ tgt,
+                                                               const TIn *__restrict__ drf, int T, int V, int ns,
+                                                               float inv_tau, const Pick *__restrict__ pick,
+                                                               const float *__restrict__ mass,
+                                                               const float *__restrict__ u_sample,
+                                                               int32_t *__restrict__ next) {
+    const int b = blockIdx.x, tid = threadIdx.x;
+    const Pick pk = pick[b];
+    __shared__ int s_slice;
+    __shared__ float s_rem;
+    __shared__ float tsum[kThreads];
+    __shared__ int s_found, s_lastpos;
+    // The slice: cumulative slice masses in slice order (one thread, in order).
+    if (tid == 0) {
+        const float *mb = mass + size_t(b) * ns;
+        float total = 0.f;
+        for (int s = 0; s < ns; ++s) total += mb[s];
+        const float t = u_sample[b] * total;
+        int sl = -1, lastpos = -1;
+        float run = 0.f, rem = 0.f;
+        for (int s = 0; s < ns; ++s) {
+            if (mb[s] > 0.f) lastpos = s;
+            if (sl < 0 && run + mb[s] > t) {
+                sl = s;
+                rem = t - run;
+            }
+            run += mb[s];
+        }
+        if (sl < 0) {   // rounding put u * total at or past the end: the last slice with weight
+            sl = lastpos;
+            rem = INFINITY;
+        }
+        s_slice = sl;
+        s_rem = rem;
+        s_found = INT_MAX;
+        s_lastpos = -1;
+    }
+    __syncthreads();
+    const int sl = s_slice;
+    if (sl < 0) {   // the weights sum to zero: the target row's argmax
+        if (tid == 0) next[b] = pk.amax;
+        return;
+    }
+    // Within the slice: thread j owns entries lo + j kPer .. + kPer - 1, in order.
+    const TIn *trow = tgt + (size_t(b) * T + pk.row) * V;
+    const TIn *drow = pk.residual ? drf + (size_t(b) * (T - 1) + pk.row) * V : nullptr;
+    const int lo = sl * kSlice + tid * kPer, hi = min(V, sl * kSlice + kSlice);
+    float w[kPer], mine = 0.f;
+    int lastpos = -1;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int i = lo + k;
+        w[k] = i < hi ? draw_weight(trow, drow, pk, inv_tau, i) : 0.f;
+        mine += w[k];
+        if (w[k] > 0.f) lastpos = i;
+    }
+    tsum[tid] = mine;
+    __syncthreads();
+    // Exclusive prefix of the thread sums (serial over the threads below: 256
+    // adds at most, in index order).
+    float excl = 0.f;
+    for (int j = 0; j < tid; ++j) excl += tsum[j];
+    // The owner is the thread whose share of the cumulative weight covers rem,
+    // tested with the same sums the next thread's prefix is made of; it takes
+    // its first entry whose running sum passes rem, or (rounding) its last entry
+    // with weight.
+    const float rem = s_rem;
+    if (excl <= rem && rem < excl + mine) {
+        float run = excl;
+        int pickd = lastpos;
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            run += w[k];
+            if (run > rem && w[k] > 0.f) {
+                pickd = lo + k;
+                break;
+            }
+        }
+        atomicMin(&s_found, pickd);
+    }
+    if (lastpos >= 0) atomicMax(&s_lastpos, lastpos);
+    __syncthreads();
+    if (tid == 0) {
+        const int x = s_found != INT_MAX ? s_found : s_lastpos;
+        next[b] = x >= 0 ? x : pk.amax;
+    }
+}
+
+// Filter history rewind: thread per channel, the new window assembled in
+// registers before it is written back.
+template <typename E>
+__global__ __launch_bounds__(256) void history_rewind_kernel(E *__restrict__ hist, const E *__restrict__ rows,
+                                                             const int32_t *__restrict__ n, int W, int T, int C) {
+    constexpr int kMaxW = GDN_HISTORY_MAX;
+    const int c = blockIdx.x * 256 + threadIdx.x, b = blockIdx.y;
+    if (c >= C) return;
+    const int nn = n[b];
+    if (nn < 0 || nn > T) return;   // out of range: the history is left as it was
+    E v[kMaxW];
+#pragma unroll
+    for (int j = 0; j < kMaxW; ++j) {
+        if (j < W) {
+            const int k = j + nn;   // index in [history; rows 0 .. n-1]
+            v[j] = k < W ? hist[(size_t(b) * W + k) * C + c] : rows[(size_t(b) * T + (k - W)) * C + c];
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxW; ++j)
+        if (j < W) hist[(size_t(b) * W + j) * C + c] = v[j];
+}
+
+struct AcceptWs {
+    size_t parts, pick, mass, total;
+};
+
+AcceptWs accept_ws_layout(int B, int T, int V, bool sampled) {
+    const int ns = (V + kSlice - 1) / kSlice, rows = sampled ? 2 * T - 1 : T;
+    AcceptWs w;
+    w.parts = 0;
+    w.pick = w.parts + align256(size_t(B) * rows * ns * sizeof(Part));
+    w.mass = w.pick + align256(size_t(B) * sizeof(Pick));
+    w.total = w.mass + (sampled ? align256(size_t(B) * ns * sizeof(float)) : 0);
+    return w;
+}
+
+template <typename TIn>
+hipError_t accept_greedy_t(const TIn *tgt, const int32_t *drafts, int B, int T, int V, int32_t *n_out,
+                           int32_t *next, uint8_t *ws, hipStream_t st) {
+    const int ns = (V + kSlice - 1) / kSlice;
+    const AcceptWs L = accept_ws_layout(B, T, V, false);
+    Part *parts = reinterpret_cast<Part *>(ws + L.parts);
+    hipLaunchKernelGGL((accept_stats_kernel<TIn, false>), dim3(ns, T, B), dim3(kThreads), 0, st, tgt,
+                       static_cast<const TIn *>(nullptr), T, V, ns, 1.f, parts);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((accept_decide_kernel<TIn, false>), dim3(B), dim3(64), 0, st, tgt,
+                       static_cast<const TIn *>(nullptr), drafts, static_cast<const float *>(nullptr), T, V, ns,
+                       1.f, parts, reinterpret_cast<Pick *>(ws + L.pick), n_out, next);
+    return hipGetLastError();
+}
+
+template <typename TIn>
+hipError_t accept_sampled_t(const TIn *tgt, const TIn *drf, const int32_t *drafts, const float *u_acc,
+                            const float *u_samp, float inv_tau, int B, int T, int V, int32_t *n_out,
+                            int32_t *next, uint8_t *ws, hipStream_t st) {
+    const int ns = (V + kSlice - 1) / kSlice;
+    const AcceptWs L = accept_ws_layout(B, T, V, true);
+    Part *parts = reinterpret_cast<Part *>(ws + L.parts);
+    Pick *pick = reinterpret_cast<Pick *>(ws + L.pick);
+    float *mass = reinterpret_cast<float *>(ws + L.mass);
+    hipLaunchKernelGGL((accept_stats_kernel<TIn, true>), dim3(ns, 2 * T - 1, B), dim3(kThreads), 0, st, tgt, drf, T,
+                       V, ns, inv_tau, parts);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((accept_decide_kernel<TIn, true>), dim3(B), dim3(64), 0, st, tgt, drf, drafts, u_acc, T, V,
+                       ns, inv_tau, parts, pick, n_out, static_cast<int32_t *>(nullptr));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((accept_mass_kernel<TIn>), dim3(ns, B), dim3(kThreads), 0, st, tgt, drf, T, V, ns, inv_tau,
+                       pick, mass);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((accept_pick_kernel<TIn>), dim3(B), dim3(kThreads), 0, st, tgt, drf, T, V, ns, inv_tau,
+                       pick, mass, u_samp, next);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t accept_workspace_bytes(int B, int T, int V, bool sampled) {
+    return accept_ws_layout(B, T, V, sampled).total;
+}
+
+hipError_t launch_accept_greedy(const void *tgt, gdn_in_dtype dt, const int32_t *drafts, int B, int T, int V,
+                                int32_t *n_out, int32_t *next, void *ws, hipStream_t st) {
+    uint8_t *w = static_cast<uint8_t *>(ws);
+    if (dt == GDN_IN_BF16)
+        return accept_greedy_t(static_cast<const __hip_bfloat16 *>(tgt), drafts, B, T, V, n_out, next, w, st);
+    return accept_greedy_t(static_cast<const float *>(tgt), drafts, B, T, V, n_out, next, w, st);
+}
+
+hipError_t launch_accept_sampled(const void *tgt, const void *drf, gdn_in_dtype dt, const int32_t *drafts,
+                                 const float *u_acc, const float *u_samp, float inv_tau, int B, int T, int V,
+                                 int32_t *n_out, int32_t *next, void *ws, hipStream_t st) {
+    uint8_t *w = static_cast<uint8_t *>(ws);
+    if (dt == GDN_IN_BF16)
+        return accept_sampled_t(static_cast<const __hip_bfloat16 *>(tgt), static_cast<const __hip_bfloat16 *>(drf),
+                                drafts, u_acc, u_samp, inv_tau, B, T, V, n_out, next, w, st);
+    return accept_sampled_t(static_cast<const float *>(tgt), static_cast<const float *>(drf), drafts, u_acc, u_samp,
+                            inv_tau, B, T, V, n_out, next, w, st);
+}
+
+hipError_t launch_history_rewind(void *hist, const void *rows, const int32_t *n, int B, int W, int T, int C,
+                                 gdn_in_dtype dt, hipStream_t st) {
+    const dim3 grid((C + 255) / 256, B);
+    if (dt == GDN_IN_BF16)
+        hipLaunchKernelGGL((history_rewind_kernel<uint16_t>), grid, dim3(256), 0, st, static_cast<uint16_t *>(hist),
+                           static_cast<const uint16_t *>(rows), n, W, T, C);
+    else
+        hipLaunchKernelGGL((history_rewind_kernel<uint32_t>), grid, dim3(256), 0, st, static_cast<uint32_t *>(hist),
+                           static_cast<const uint32_t *>(rows), n, W, T, C);
+    return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -5,6 +5,8 @@
 
 #include <vector>
 
+#include <cmath>
+
 #include "gdn_internal.h"
 
 using namespace gdn;
@@ -24,6 +26,16 @@ int check_shape(const gdn_shape *s) {
 bool valid_dtype(int dt) { return dt == GDN_IN_F32 || dt == GDN_IN_BF16; }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_EHIP; }
+
+constexpr int32_t kVocabMax = 1 << 26;
+
+int check_accept_shape(const gdn_accept_shape *s) {
+    if (s == nullptr) return GDN_EINVAL;
+    if (s->B < 1 || s->B > 65535 || s->V < 1 || s->V > kVocabMax) return GDN_EDIM;
+    if (s->T < 1 || s->T > GDN_T_MAX) return GDN_ERANGE;
+    if (int64_t(s->B) * s->T * s->V > (int64_t(1) << 40)) return GDN_EDIM;
+    return GDN_OK;
+}
 
 }  // namespace
 
@@ -118,6 +130,57 @@ int gdn_prefill_chunked(float *S, const void *q, const void *k, const void *v, c
     if (int64_t(L) * shp->B * shp->H > int64_t(INT_MAX)) return GDN_EDIM;
     return hip_status(launch_prefill(S, q, k, v, g, beta, L, in_dt, *shp, o, ws, ws_bytes,
                                      static_cast<hipStream_t>(hip_stream)));
+}
+
+size_t gdn_accept_workspace_bytes(const gdn_accept_shape *shp, int32_t sampled) {
+    if (check_accept_shape(shp) != GDN_OK) return 0;
+    return accept_workspace_bytes(shp->B, shp->T, shp->V, sampled != 0);
+}
+
+int gdn_accept_greedy(const void *target_logits, gdn_in_dtype dt, const int32_t *draft_tokens,
+                      const gdn_accept_shape *shp, int32_t *n_out, int32_t *next_token, void *ws,
+                      size_t ws_bytes, void *hip_stream) {
+    int rc = check_accept_shape(shp);
+    if (rc != GDN_OK) return rc;
+    if (!valid_dtype(dt)) return GDN_EINVAL;
+    if (!aligned(target_logits, size_t(esize_of(dt))) || !aligned(n_out, 4) || !aligned(next_token, 4) ||
+        !aligned(ws, 16))
+        return GDN_EINVAL;
+    if (shp->T > 1 && !aligned(draft_tokens, 4)) return GDN_EINVAL;
+    if (ws_bytes < accept_workspace_bytes(shp->B, shp->T, shp->V, false)) return GDN_EWS;
+    return hip_status(launch_accept_greedy(target_logits, dt, draft_tokens, shp->B, shp->T, shp->V, n_out,
+                                           next_token, ws, static_cast<hipStream_t>(hip_stream)));
+}
+
+int gdn_accept_sampled(const void *target_logits, const void *draft_logits, gdn_in_dtype dt,
+                       const int32_t *draft_tokens, const float *u_accept, const float *u_sample,
+                       float temperature, const gdn_accept_shape *shp, int32_t *n_out, int32_t *next_token,
+                       void *ws, size_t ws_bytes, void *hip_stream) {
+    int rc = check_accept_shape(shp);
+    if (rc != GDN_OK) return rc;
+    if (!valid_dtype(dt)) return GDN_EINVAL;
+    if (!(temperature > 0.f) || !std::isfinite(temperature)) return GDN_ERANGE;
+    const size_t es = size_t(esize_of(dt));
+    if (!aligned(target_logits, es) || !aligned(u_sample, 4) || !aligned(n_out, 4) || !aligned(next_token, 4) ||
+        !aligned(ws, 16))
+        return GDN_EINVAL;
+    if (shp->T > 1 && (!aligned(draft_logits, es) || !aligned(draft_tokens, 4) || !aligned(u_accept, 4)))
+        return GDN_EINVAL;
+    if (ws_bytes < accept_workspace_bytes(shp->B, shp->T, shp->V, true)) return GDN_EWS;
+    return hip_status(launch_accept_sampled(target_logits, draft_logits, dt, draft_tokens, u_accept, u_sample,
+                                            1.f / temperature, shp->B, shp->T, shp->V, n_out, next_token, ws,
+                                            static_cast<hipStream_t>(hip_stream)));
+}
+
+int gdn_history_rewind(void *history, const void *rows, const int32_t *n, int32_t B, int32_t W, int32_t T,
+                       int32_t C, gdn_in_dtype dt, void *hip_stream) {
+    if (!valid_dtype(dt)) return GDN_EINVAL;
+    if (B < 1 || C < 1 || B > 65535) return GDN_EDIM;
+    if (W < 1 || W > GDN_HISTORY_MAX || T < 1 || T > GDN_T_MAX) return GDN_ERANGE;
+    const size_t es = size_t(esize_of(dt));
+    if (!aligned(history, es) || !aligned(rows, es) || !aligned(n, 4)) return GDN_EINVAL;
+    return hip_status(
+        launch_history_rewind(history, rows, n, B, W, T, C, dt, static_cast<hipStream_t>(hip_stream)));
 }
 
 const char *gdn_strerror(int status) {

@@ -195,5 +195,13 @@ hipError_t launch_prefill(float *S, const void *q, const void *k, const void *v,
 // Workspace bytes the two-pass prefill schedule uses for this shape and prompt
 // length (0 when the one-pass schedule is the faster one).
 size_t prefill_workspace_bytes(const gdn_shape &shp, int L);
+size_t accept_workspace_bytes(int B, int T, int V, bool sampled);
+hipError_t launch_accept_greedy(const void *tgt, gdn_in_dtype dt, const int32_t *drafts, int B, int T, int V,
+                                int32_t *n_out, int32_t *next, void *ws, hipStream_t st);
+hipError_t launch_accept_sampled(const void *tgt, const void *drf, gdn_in_dtype dt, const int32_t *drafts,
+                                 const float *u_acc, const float *u_samp, float inv_tau, int B, int T, int V,
+                                 int32_t *n_out, int32_t *next, void *ws, hipStream_t st);
+hipError_t launch_history_rewind(void *hist, const void *rows, const int32_t *n, int B, int W, int T, int C,
+                                 gdn_in_dtype dt, hipStream_t st);
 
 }  // namespace gdn

@@ -32,8 +32,13 @@ EXPORTED = (
     "gdn_record_status",
     "gdn_prefill_workspace_bytes",
     "gdn_prefill_chunked",
+    "gdn_accept_workspace_bytes",
+    "gdn_accept_greedy",
+    "gdn_accept_sampled",
+    "gdn_history_rewind",
     "gdn_strerror",
 )
+GDN_HISTORY_MAX = 16
 
 
 class GdnError(RuntimeError):
@@ -45,6 +50,10 @@ class GdnError(RuntimeError):
 class gdn_shape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("dk", ctypes.c_int32),
                 ("dv", ctypes.c_int32)]
+
+
+class gdn_accept_shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("V", ctypes.c_int32)]
 
 
 def _load() -> ctypes.CDLL:
@@ -67,6 +76,15 @@ def _load() -> ctypes.CDLL:
     lib.gdn_prefill_workspace_bytes.argtypes = [sp, i32, i32]
     lib.gdn_prefill_chunked.restype = ctypes.c_int
     lib.gdn_prefill_chunked.argtypes = [vp] * 6 + [i32, i32, ctypes.c_int, sp, vp, vp, sz, vp]
+    ap = ctypes.POINTER(gdn_accept_shape)
+    lib.gdn_accept_workspace_bytes.restype = sz
+    lib.gdn_accept_workspace_bytes.argtypes = [ap, i32]
+    lib.gdn_accept_greedy.restype = ctypes.c_int
+    lib.gdn_accept_greedy.argtypes = [vp, ctypes.c_int, vp, ap, vp, vp, vp, sz, vp]
+    lib.gdn_accept_sampled.restype = ctypes.c_int
+    lib.gdn_accept_sampled.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp, ctypes.c_float, ap, vp, vp, vp, sz, vp]
+    lib.gdn_history_rewind.restype = ctypes.c_int
+    lib.gdn_history_rewind.argtypes = [vp, vp, vp, i32, i32, i32, i32, ctypes.c_int, vp]
     lib.gdn_strerror.restype = ctypes.c_char_p
     lib.gdn_strerror.argtypes = [ctypes.c_int]
     return lib
@@ -216,3 +234,84 @@ def gdn_prefill_chunked(S, q, k, v, g, beta, o, chunk: int = GDN_PREFILL_CHUNK, 
                                  _stream(stream))
     if rc != 0:
         raise GdnError(rc, "gdn_prefill_chunked")
+
+
+def _accept_shape(target_logits) -> gdn_accept_shape:
+    if target_logits.dim() != 3:
+        raise ValueError("target_logits must be [B][T][V]")
+    B, T, V = target_logits.shape
+    return gdn_accept_shape(B, T, V)
+
+
+def _check_accept(shp, draft_tokens, n_out, next_token):
+    B, T = shp.B, shp.T
+    if T > 1 and (draft_tokens is None or tuple(draft_tokens.shape) != (B, T - 1)
+                  or draft_tokens.dtype != torch.int32):
+        raise ValueError("draft_tokens must be int32 [B][T-1]")
+    for name, x in (("n_out", n_out), ("next_token", next_token)):
+        if tuple(x.shape) != (B,) or x.dtype != torch.int32:
+            raise ValueError(f"{name} must be int32 [B]")
+
+
+def gdn_accept_workspace_bytes(target_logits, sampled: bool) -> int:
+    return int(lib.gdn_accept_workspace_bytes(ctypes.byref(_accept_shape(target_logits)), int(bool(sampled))))
+
+
+def _accept_ws(shp, sampled, device, ws):
+    if ws is None:
+        need = int(lib.gdn_accept_workspace_bytes(ctypes.byref(shp), int(sampled)))
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+    return ws, ws.numel() * ws.element_size()
+
+
+def gdn_accept_greedy(target_logits, draft_tokens, n_out, next_token, ws=None, stream=None) -> None:
+    """Greedy acceptance of one verify block per sequence, on the device: n_out[b]
+    = 1 + drafts kept, next_token[b] = the emitted (correction or bonus) token.
+    ``ws`` is the workspace of gdn_accept_workspace_bytes(target_logits, False)
+    bytes; when None it is allocated here (device memory only)."""
+    shp = _accept_shape(target_logits)
+    _check_accept(shp, draft_tokens, n_out, next_token)
+    ws, nb = _accept_ws(shp, False, target_logits.device, ws)
+    rc = lib.gdn_accept_greedy(_ptr(target_logits), _dt(target_logits), _ptr(draft_tokens), ctypes.byref(shp),
+                               _ptr(n_out), _ptr(next_token), _ptr(ws), nb, _stream(stream))
+    if rc != 0:
+        raise GdnError(rc, "gdn_accept_greedy")
+
+
+def gdn_accept_sampled(target_logits, draft_logits, draft_tokens, u_accept, u_sample, temperature, n_out,
+                       next_token, ws=None, stream=None) -> None:
+    """Exact speculative sampling of one verify block per sequence, on the device
+    (see gdn_accept_sampled in include/gdn.h)."""
+    shp = _accept_shape(target_logits)
+    _check_accept(shp, draft_tokens, n_out, next_token)
+    B, T, V = shp.B, shp.T, shp.V
+    if T > 1:
+        if tuple(draft_logits.shape) != (B, T - 1, V) or draft_logits.dtype != target_logits.dtype:
+            raise ValueError("draft_logits must be [B][T-1][V] in the target logits' dtype")
+        if tuple(u_accept.shape) != (B, T - 1) or u_accept.dtype != torch.float32:
+            raise ValueError("u_accept must be float32 [B][T-1]")
+    if tuple(u_sample.shape) != (B,) or u_sample.dtype != torch.float32:
+        raise ValueError("u_sample must be float32 [B]")
+    ws, nb = _accept_ws(shp, True, target_logits.device, ws)
+    rc = lib.gdn_accept_sampled(_ptr(target_logits), _ptr(draft_logits if T > 1 else None), _dt(target_logits),
+                                _ptr(draft_tokens if T > 1 else None), _ptr(u_accept if T > 1 else None),
+                                _ptr(u_sample), float(temperature), ctypes.byref(shp), _ptr(n_out),
+                                _ptr(next_token), _ptr(ws), nb, _stream(stream))
+    if rc != 0:
+        raise GdnError(rc, "gdn_accept_sampled")
+
+
+def gdn_history_rewind(history, rows, n, stream=None) -> None:
+    """history [B][W][C] (in place) becomes the last W rows of [history; rows[:, :n]]
+    per sequence; rows [B][T][C] in history's dtype; n int32 [B] on the device."""
+    if history.dim() != 3 or rows.dim() != 3:
+        raise ValueError("history must be [B][W][C] and rows [B][T][C]")
+    B, W, C = history.shape
+    if rows.shape[0] != B or rows.shape[2] != C or rows.dtype != history.dtype:
+        raise ValueError("rows must be [B][T][C] in history's dtype")
+    if tuple(n.shape) != (B,) or n.dtype != torch.int32:
+        raise ValueError("n must be int32 [B]")
+    rc = lib.gdn_history_rewind(_ptr(history), _ptr(rows), _ptr(n), B, W, rows.shape[1], C, _dt(history),
+                                _stream(stream))
+    if rc != 0:
+        raise GdnError(rc, "gdn_history_rewind")

@@ -76,3 +76,82 @@ def make_accepts(count: int, T: int, *, seed: int = 0) -> torch.Tensor:
     gen = torch.Generator()
     gen.manual_seed(int(seed) + 7919)
     return torch.randint(0, T + 1, (count,), generator=gen, dtype=torch.int32)
+
+
+# ---------------------------------------------------------------------------
+# Acceptance inputs: logits of one verify block per sequence, standing in for a
+# target model and its drafter (no weights or vocabulary file involved).
+#
+#   target logits  N(0,1) per entry, plus `peak` on `n_peak` random entries per
+#                  row (a few likely tokens over a flat tail, the shape of a
+#                  language model's next-token distribution)
+#   drafter logits the target's rows 0 .. T-2 plus drift * N(0,1) (a drafter
+#                  close to its target)
+#   draft tokens   drawn from softmax(drafter / tau) by the Gumbel-max rule:
+#                  argmax(drafter / tau - log(-log U)), U uniform
+#   u_accept, u_sample   U[0, 1)
+# With ``plan_greedy`` each sequence instead draws k ~ Uniform{0..T-1}; row j
+# gets a planted top entry (one random entry raised to 1 above the row's
+# maximum), drafts j < k copy it and draft k (when k < T - 1) is another entry.
+# Logits are rounded to ``dtype`` last.  Draw order: target, peaks, drafter,
+# Gumbel noise, u_accept, u_sample (or target, plan).
+# ---------------------------------------------------------------------------
+@dataclass
+class AcceptInputs:
+    target: torch.Tensor     # [B][T][V]
+    draft: torch.Tensor      # [B][T-1][V]
+    tokens: torch.Tensor     # int32 [B][T-1]
+    u_accept: torch.Tensor   # fp32 [B][T-1]
+    u_sample: torch.Tensor   # fp32 [B]
+
+    def to(self, device) -> "AcceptInputs":
+        return AcceptInputs(*(getattr(self, f).to(device)
+                              for f in ("target", "draft", "tokens", "u_accept", "u_sample")))
+
+
+def make_accept_inputs(B: int, T: int, V: int, *, dtype=torch.bfloat16, seed: int = 0, device="cpu",
+                       tau: float = 1.0, peak: float = 8.0, n_peak: int = 4, drift: float = 0.5,
+                       plan_greedy: bool = False) -> AcceptInputs:
+    gen = torch.Generator()
+    gen.manual_seed(int(seed) + 104729)
+    f32 = torch.float32
+    target = torch.randn(B, T, V, generator=gen, dtype=f32)
+    if plan_greedy:
+        k = torch.randint(0, T, (B,), generator=gen)
+        top = torch.randint(0, V, (B, T), generator=gen)
+        other = torch.randint(0, max(V - 1, 1), (B, T), generator=gen)
+        rmax = target.max(dim=2).values
+        target.scatter_(2, top.unsqueeze(2), (rmax + 1.0).unsqueeze(2))
+        tokens = torch.empty(B, max(T - 1, 0), dtype=torch.int32)
+        for b in range(B):
+            for j in range(T - 1):
+                if j < int(k[b]):
+                    tokens[b, j] = top[b, j]
+                else:   # any entry but the planted one
+                    o = int(other[b, j])
+                    tokens[b, j] = o + 1 if o >= int(top[b, j]) and V > 1 else o
+        draft = target[:, : T - 1].clone()
+        u_acc = torch.zeros(B, max(T - 1, 0), dtype=f32)
+        u_smp = torch.zeros(B, dtype=f32)
+    else:
+        if n_peak > 0 and peak != 0.0:
+            idx = torch.randint(0, V, (B, T, n_peak), generator=gen)
+            target.scatter_add_(2, idx, torch.full((B, T, n_peak), float(peak)))
+        draft = target[:, : T - 1] + drift * torch.randn(B, max(T - 1, 0), V, generator=gen, dtype=f32)
+        draft = draft.to(dtype).to(f32)
+        gum = -torch.log(-torch.log(torch.rand(B, max(T - 1, 0), V, generator=gen, dtype=f32).clamp_min(1e-30)))
+        tokens = torch.argmax(draft / tau + gum, dim=2).to(torch.int32)
+        u_acc = torch.rand(B, max(T - 1, 0), generator=gen, dtype=f32)
+        u_smp = torch.rand(B, generator=gen, dtype=f32)
+    out = AcceptInputs(target.to(dtype).contiguous(), draft.to(dtype).contiguous(), tokens.contiguous(),
+                       u_acc.contiguous(), u_smp.contiguous())
+    return out.to(device)
+
+
+def make_history_inputs(B: int, W: int, T: int, C: int, *, dtype=torch.bfloat16, seed: int = 0, device="cpu"):
+    """Filter history [B][W][C] and the block's filter inputs [B][T][C], N(0,1)."""
+    gen = torch.Generator()
+    gen.manual_seed(int(seed) + 1299709)
+    hist = torch.randn(B, W, C, generator=gen).to(dtype)
+    rows = torch.randn(B, T, C, generator=gen).to(dtype)
+    return hist.to(device), rows.to(device)

@@ -120,3 +120,56 @@ def test_record_size_accounts_for_payload(G):
     # Many heads: one pass, no workspace.
     assert G.lib.gdn_prefill_workspace_bytes(_shape(B=48, H=32, dk=128, dv=128), 4096, 64) == 0
     assert G.lib.gdn_prefill_workspace_bytes(_shape(), 4096, 32) == 0
+
+
+def _ashape(B=1, T=8, V=1000):
+    import speculative_verify_amd.gdn as G
+    return ctypes.byref(G.gdn_accept_shape(B, T, V))
+
+
+def test_accept_and_rewind_reject_bad_arguments(G):
+    L = G.lib
+    big = 1 << 30
+    ok = dict(tgt=FAKE, dt=1, drafts=FAKE, shp=None, n=FAKE, nxt=FAKE, ws=FAKE, wsb=big)
+
+    def greedy(**kw):
+        a = {**ok, **kw}
+        return L.gdn_accept_greedy(a["tgt"], a["dt"], a["drafts"], a["shp"] or _ashape(), a["n"], a["nxt"],
+                                   a["ws"], a["wsb"], None)
+
+    assert greedy(tgt=None) == -1
+    assert greedy(dt=7) == -1
+    assert greedy(drafts=None) == -1
+    assert greedy(ws=FAKE_ODD) == -1
+    assert greedy(shp=_ashape(B=0)) == -2
+    assert greedy(shp=_ashape(V=0)) == -2
+    assert greedy(shp=_ashape(V=(1 << 26) + 1)) == -2
+    assert greedy(shp=_ashape(T=0)) == -3
+    assert greedy(shp=_ashape(T=17)) == -3
+    assert greedy(wsb=16) == -4
+    # T = 1: no drafts needed; still refused here for the workspace only.
+    assert greedy(drafts=None, shp=_ashape(T=1), wsb=16) == -4
+
+    def sampled(temp=1.0, wsb=big, draft=FAKE, shp=None):
+        return L.gdn_accept_sampled(FAKE, draft, 1, FAKE, FAKE, FAKE, temp, shp or _ashape(), FAKE, FAKE, FAKE,
+                                    wsb, None)
+
+    assert sampled(temp=0.0) == -3
+    assert sampled(temp=-1.0) == -3
+    assert sampled(temp=float("inf")) == -3
+    assert sampled(temp=float("nan")) == -3
+    assert sampled(draft=None) == -1
+    assert sampled(wsb=64) == -4
+    assert L.gdn_accept_workspace_bytes(_ashape(), 1) > L.gdn_accept_workspace_bytes(_ashape(), 0) > 0
+    assert L.gdn_accept_workspace_bytes(_ashape(T=0), 0) == 0
+
+    def rewind(B=1, W=3, T=8, C=16, dt=1, hist=FAKE):
+        return L.gdn_history_rewind(hist, FAKE, FAKE, B, W, T, C, dt, None)
+
+    assert rewind(hist=None) == -1
+    assert rewind(dt=5) == -1
+    assert rewind(B=0) == -2
+    assert rewind(C=0) == -2
+    assert rewind(W=0) == -3
+    assert rewind(W=17) == -3
+    assert rewind(T=17) == -3
