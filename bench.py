@@ -48,6 +48,7 @@ def parse():
     p.add_argument("--prefill-reps", type=int, default=20)
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--no-accept", action="store_true")
     p.add_argument("--decode-steps", type=int, default=10000)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget-s", type=float, default=15.0)
@@ -398,6 +399,8 @@ def main():
         result["prefill"] = bench_prefill(args, G, dev)
     if not args.no_decode:
         result["decode"] = bench_decode(args, G, dev)
+    if not args.no_accept:
+        result["accept"] = bench_accept(args, G, dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args)
     if args.copy_calibration_mib > 0:
@@ -631,6 +634,81 @@ def bench_decode(args, G, dev):
             "algorithmic_bytes_per_step": nbytes,
             "effective_GBs_graph": round(nbytes / (graph_us * 1e-6) / 1e9, 1),
             "note": "state cache-resident between steps"}
+
+
+ACC_V = 151936   # the Qwen3 tokenizer's vocabulary (the pages' targets are Qwen3-family models)
+HIST_C = 8192    # filter channels of one GDN layer: q, k (16 heads x 128) and v (32 heads x 128)
+HIST_W = 3       # history rows of a width-4 causal filter
+
+
+def accept_bytes(B, T, V, es, sampled):
+    """Algorithmic HBM bytes of one acceptance call: every target row (and, when
+    sampled, every drafter row) read once, the draft tokens and uniforms read and
+    n and the emitted token written."""
+    rows = 2 * T - 1 if sampled else T
+    return B * rows * V * es + B * (T - 1) * (8 if sampled else 4) + B * (12 if sampled else 8)
+
+
+def bench_accept(args, G, dev):
+    """On-device acceptance of one verify block (one sequence, T = 8 rows, the
+    Qwen3 vocabulary, bf16 logits), greedy and sampled, and the filter-history
+    rewind of all 48 GDN layers (history [48][3][8192] bf16).  Each timed over
+    200 calls back to back, eagerly and as a HIP graph of 20 calls."""
+    import torch
+
+    from speculative_verify_amd.inputs import make_accept_inputs, make_history_inputs
+
+    B, Tb, V = 1, T, ACC_V
+    x = make_accept_inputs(B, Tb, V, dtype=torch.bfloat16, seed=args.seed + 55, device=dev, peak=16.0)
+    n = torch.empty(B, dtype=torch.int32, device=dev)
+    nxt = torch.empty(B, dtype=torch.int32, device=dev)
+    wg = torch.empty(G.gdn_accept_workspace_bytes(x.target, False), dtype=torch.uint8, device=dev)
+    wsamp = torch.empty(G.gdn_accept_workspace_bytes(x.target, True), dtype=torch.uint8, device=dev)
+    hist, rows = make_history_inputs(LAYERS, HIST_W, Tb, HIST_C, seed=args.seed + 56, device=dev)
+    nh = torch.full((LAYERS,), 5, dtype=torch.int32, device=dev)
+    calls = {
+        "greedy": lambda: G.gdn_accept_greedy(x.target, x.tokens, n, nxt, ws=wg),
+        "sampled": lambda: G.gdn_accept_sampled(x.target, x.draft, x.tokens, x.u_accept, x.u_sample, 1.0, n, nxt,
+                                                ws=wsamp),
+        "history_rewind": lambda: G.gdn_history_rewind(hist, rows, nh),
+    }
+    nbytes = {"greedy": accept_bytes(B, Tb, V, 2, False), "sampled": accept_bytes(B, Tb, V, 2, True),
+              "history_rewind": LAYERS * HIST_C * 2 * 2 * HIST_W + LAYERS * 4}   # W rows read, W written
+    out = {"workload": f"acceptance of one verify block: 1 sequence, T={Tb} rows (anchor + {Tb - 1} drafts), "
+                       f"V={V}, bf16 logits; filter-history rewind of {LAYERS} layers x {HIST_W} rows x "
+                       f"{HIST_C} channels, bf16, n=5"}
+    N, GS = 200, 20
+    for name, fn in calls.items():
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(N):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        eager = a.elapsed_time(b) / N * 1e3
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                for _ in range(GS):
+                    fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(N // GS):
+            graph.replay()
+        b.record()
+        torch.cuda.synchronize()
+        gus = a.elapsed_time(b) / N * 1e3
+        out[name] = {"us_per_call_eager": round(eager, 2), "us_per_call_graph": round(gus, 2),
+                     "algorithmic_bytes": nbytes[name],
+                     "effective_GBs_graph": round(nbytes[name] / (gus * 1e-6) / 1e9, 1)}
+    return out
 
 
 def bench_prefill(args, G, dev):

@@ -142,51 +142,89 @@ __global__ __launch_bounds__(kThreads) void accept_stats_kernel(const TIn *__res
     }
 }
 
-// One wave per sequence: combine the slices of every row, then walk the drafts.
+constexpr int kPartChunk = 2048;   // (row, slice) statistics staged in LDS at a time
+
+// One workgroup per sequence: combine the slices of every row (all statistics
+// loaded at once into LDS, then one row per wave), then walk the drafts.
 template <typename TIn, bool SAMPLED>
-__global__ __launch_bounds__(64) void accept_decide_kernel(
+__global__ __launch_bounds__(kThreads) void accept_decide_kernel(
     const TIn *__restrict__ tgt, const TIn *__restrict__ drf, const int32_t *__restrict__ drafts,
     const float *__restrict__ u_acc, int T, int V, int ns, float inv_tau, const Part *__restrict__ parts,
     Pick *__restrict__ pick, int32_t *__restrict__ n_out, int32_t *__restrict__ next) {
-    const int b = blockIdx.x, lane = threadIdx.x;
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int rows = SAMPLED ? 2 * T - 1 : T;
-    __shared__ float M[2 * GDN_T_MAX], S[2 * GDN_T_MAX];
+    __shared__ Part stage[kPartChunk];
+    __shared__ float M[2 * GDN_T_MAX], S[2 * GDN_T_MAX], BV[2 * GDN_T_MAX];
     __shared__ int AM[2 * GDN_T_MAX];
-    for (int r = 0; r < rows; ++r) {
-        const Part *pr = parts + (size_t(b) * rows + r) * ns;
-        float m = -INFINITY, s = 0.f, bv = -INFINITY;
-        int bi = INT_MAX;
-        for (int j = lane; j < ns; j += 64) {
-            const Part p = pr[j];
-            amax_merge(bv, bi, p.bv, p.bi);
-            if constexpr (SAMPLED) lse_merge(m, s, p.m, p.s);
+    if (tid < rows) {
+        M[tid] = -INFINITY;
+        S[tid] = 0.f;
+        BV[tid] = -INFINITY;
+        AM[tid] = INT_MAX;
+    }
+    // Every draft token, its uniform and (sampled) its two logits, fetched by one
+    // lane each first (their loads overlap the staging below), so the walk reads only LDS.
+    __shared__ int D[GDN_T_MAX];
+    __shared__ float U[GDN_T_MAX], ZT[GDN_T_MAX], ZD[GDN_T_MAX];
+    if (tid < T - 1) {
+        const int d = drafts[size_t(b) * (T - 1) + tid];
+        D[tid] = d;
+        if constexpr (SAMPLED) {
+            const bool ok = d >= 0 && d < V;
+            U[tid] = u_acc[size_t(b) * (T - 1) + tid];
+            ZT[tid] = ok ? ld(tgt, (size_t(b) * T + tid) * V + d) : 0.f;
+            ZD[tid] = ok ? ld(drf, (size_t(b) * (T - 1) + tid) * V + d) : 0.f;
         }
+    }
+    const Part *pb = parts + size_t(b) * rows * ns;
+    // Rows are walked in groups whose statistics fit the stage.
+    const int rpc = max(1, kPartChunk / ns);            // whole rows per stage
+    for (int r0 = 0; r0 < rows; r0 += rpc) {
+        const int nr = min(rpc, rows - r0);
+        for (int s0 = 0; s0 < ns; s0 += kPartChunk) {   // (a row longer than the stage: in pieces)
+            const int sn = min(kPartChunk, ns - s0);
+            const int cnt = nr == 1 ? sn : nr * ns;
+            __syncthreads();
+            for (int e = tid; e < cnt; e += kThreads) {
+                const int rr = nr == 1 ? 0 : e / ns, jj = nr == 1 ? s0 + e : e - rr * ns;
+                stage[e] = pb[size_t(r0 + rr) * ns + jj];
+            }
+            __syncthreads();
+            for (int rr = w; rr < nr; rr += kThreads / 64) {
+                float m = -INFINITY, sm = 0.f, bv = -INFINITY;
+                int bi = INT_MAX;
+                const int len = nr == 1 ? sn : ns;
+                for (int j2 = lane; j2 < len; j2 += 64) {
+                    const Part pp = stage[(nr == 1 ? 0 : rr * ns) + j2];
+                    amax_merge(bv, bi, pp.bv, pp.bi);
+                    if constexpr (SAMPLED) lse_merge(m, sm, pp.m, pp.s);
+                }
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            amax_merge(bv, bi, __shfl_xor(bv, off, 64), __shfl_xor(bi, off, 64));
-            if constexpr (SAMPLED) lse_merge(m, s, __shfl_xor(m, off, 64), __shfl_xor(s, off, 64));
-        }
-        if (lane == 0) {
-            M[r] = m;
-            S[r] = s;
-            AM[r] = bi;
+                for (int off = 32; off >= 1; off >>= 1) {
+                    amax_merge(bv, bi, __shfl_xor(bv, off, 64), __shfl_xor(bi, off, 64));
+                    if constexpr (SAMPLED) lse_merge(m, sm, __shfl_xor(m, off, 64), __shfl_xor(sm, off, 64));
+                }
+                if (lane == 0) {
+                    const int r = r0 + rr;
+                    amax_merge(BV[r], AM[r], bv, bi);
+                    if constexpr (SAMPLED) lse_merge(M[r], S[r], m, sm);
+                }
+            }
         }
     }
     __syncthreads();
-    if (lane != 0) return;
-    const int32_t *db = T > 1 ? drafts + size_t(b) * (T - 1) : nullptr;
+    if (tid != 0) return;
     int m = 0;
     if constexpr (!SAMPLED) {
-        while (m < T - 1 && db[m] == AM[m]) ++m;
+        while (m < T - 1 && D[m] == AM[m]) ++m;
         next[b] = AM[m];
     } else {
-        const float *ub = T > 1 ? u_acc + size_t(b) * (T - 1) : nullptr;
         while (m < T - 1) {
-            const int d = db[m];
+            const int d = D[m];
             if (d < 0 || d >= V) break;   // an out-of-range draft is rejected
-            const float p = __expf(ld(tgt, (size_t(b) * T + m) * V + d) * inv_tau - M[m]) / S[m];
-            const float q = __expf(ld(drf, (size_t(b) * (T - 1) + m) * V + d) * inv_tau - M[T + m]) / S[T + m];
-            if (!(ub[m] * q < p)) break;
+            const float p = __expf(ZT[m] * inv_tau - M[m]) / S[m];
+            const float q = __expf(ZD[m] * inv_tau - M[T + m]) / S[T + m];
+            if (!(U[m] * q < p)) break;
             ++m;
         }
         Pick pk;
@@ -203,126 +241,155 @@ __global__ __launch_bounds__(64) void accept_decide_kernel(
     n_out[b] = m + 1;
 }
 
-// Weight of vocabulary entry i in the draw: p(i), or max(0, p(i) - q(i)).
+// Weight of vocabulary entry i in the draw, p(i) or max(0, p(i) - q(i)) in
+// fp32, then as an integer in units of 2^-52 (the weights sum to about 1, so a
+// 64-bit total cannot overflow).  Every sum and prefix of the draw is then an
+// exact integer sum: the same in any order, in any kernel.
+constexpr double kFix = 4503599627370496.0;   // 2^52
+
 template <typename TIn>
-__device__ inline float draw_weight(const TIn *trow, const TIn *drow, const Pick &pk, float inv_tau, int i) {
+__device__ inline uint64_t draw_weight(const TIn *trow, const TIn *drow, const Pick &pk, float inv_tau, int i) {
     const float p = __expf(ld(trow, i) * inv_tau - pk.mt) / pk.st;
-    if (!pk.residual) return p;
-    const float q = __expf(ld(drow, i) * inv_tau - pk.md) / pk.sd;
-    return fmaxf(p - q, 0.f);
+    float wt = p;
+    if (pk.residual) {
+        const float q = __expf(ld(drow, i) * inv_tau - pk.md) / pk.sd;
+        wt = fmaxf(p - q, 0.f);
+    }
+    return static_cast<uint64_t>(double(wt) * kFix);
+}
+
+__device__ inline uint64_t shfl_xor_u64(uint64_t v, int off) {
+    const uint32_t lo = __shfl_xor(uint32_t(v), off, 64), hi = __shfl_xor(uint32_t(v >> 32), off, 64);
+    return (uint64_t(hi) << 32) | lo;
+}
+__device__ inline uint64_t shfl_up_u64(uint64_t v, int off) {
+    const uint32_t lo = __shfl_up(uint32_t(v), off, 64), hi = __shfl_up(uint32_t(v >> 32), off, 64);
+    return (uint64_t(hi) << 32) | lo;
+}
+
+// Exclusive prefix sum over the workgroup's threads (exact: integers).  Returns
+// this thread's exclusive prefix; *total gets the sum of all.
+__device__ inline uint64_t block_excl_scan(uint64_t v, uint64_t *total) {
+    __shared__ uint64_t wsum[kThreads / 64];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    uint64_t incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint64_t y = shfl_up_u64(incl, off);
+        if (lane >= off) incl += y;
+    }
+    __syncthreads();   // wsum free (an earlier scan may still read it)
+    if (lane == 63) wsum[w] = incl;
+    __syncthreads();
+    uint64_t base = 0, all = 0;
+#pragma unroll
+    for (int j = 0; j < kThreads / 64; ++j) {
+        if (j < w) base += wsum[j];
+        all += wsum[j];
+    }
+    *total = all;
+    return base + incl - v;
 }
 
 template <typename TIn>
 __global__ __launch_bounds__(kThreads) void accept_mass_kernel(const TIn *__restrict__ tgt,
                                                                const TIn *__restrict__ drf, int T, int V, int ns,
                                                                float inv_tau, const Pick *__restrict__ pick,
-                                                               float *__restrict__ mass) {
+                                                               uint64_t *__restrict__ mass) {
     const int s = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
     const Pick pk = pick[b];
     const TIn *trow = tgt + (size_t(b) * T + pk.row) * V;
     const TIn *drow = pk.residual ? drf + (size_t(b) * (T - 1) + pk.row) * V : nullptr;
     const int lo = s * kSlice, hi = min(V, lo + kSlice);
-    float acc = 0.f;
+    uint64_t acc = 0;
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
         const int i = lo + tid + k * kThreads;
         if (i < hi) acc += draw_weight(trow, drow, pk, inv_tau, i);
     }
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
-    __shared__ float ws[kThreads / 64];
+    for (int off = 32; off >= 1; off >>= 1) acc += shfl_xor_u64(acc, off);
+    __shared__ uint64_t ws[kThreads / 64];
     if ((tid & 63) == 0) ws[tid >> 6] = acc;
     __syncthreads();
-    if (tid == 0) mass[size_t(b) * ns + s] = (ws[0] + ws[1]) + (ws[2] + ws[3]);
+    if (tid == 0) mass[size_t(b) * ns + s] = ws[0] + ws[1] + ws[2] + ws[3];
 }
 
+// The draw: target t = floor(u * total); the slice whose cumulative mass first
+// passes t, then the entry within it.  All sums exact, so the slice's entries
+// add up to its mass and the search always ends on an entry with weight.
 template <typename TIn>
 __global__ __launch_bounds__(kThreads) void accept_pick_kernel(const TIn *__restrict__ tgt,
                                                                const TIn *__restrict__ drf, int T, int V, int ns,
                                                                float inv_tau, const Pick *__restrict__ pick,
-                                                               const float *__restrict__ mass,
+                                                               const uint64_t *__restrict__ mass,
                                                                const float *__restrict__ u_sample,
                                                                int32_t *__restrict__ next) {
     const int b = blockIdx.x, tid = threadIdx.x;
     const Pick pk = pick[b];
-    __shared__ int s_slice;
-    __shared__ float s_rem;
-    __shared__ float tsum[kThreads];
-    __shared__ int s_found, s_lastpos;
-    // The slice: cumulative slice masses in slice order (one thread, in order).
-    if (tid == 0) {
-        const float *mb = mass + size_t(b) * ns;
-        float total = 0.f;
-        for (int s = 0; s < ns; ++s) total += mb[s];
-        const float t = u_sample[b] * total;
-        int sl = -1, lastpos = -1;
-        float run = 0.f, rem = 0.f;
-        for (int s = 0; s < ns; ++s) {
-            if (mb[s] > 0.f) lastpos = s;
-            if (sl < 0 && run + mb[s] > t) {
-                sl = s;
-                rem = t - run;
-            }
-            run += mb[s];
-        }
-        if (sl < 0) {   // rounding put u * total at or past the end: the last slice with weight
-            sl = lastpos;
-            rem = INFINITY;
-        }
-        s_slice = sl;
-        s_rem = rem;
-        s_found = INT_MAX;
-        s_lastpos = -1;
-    }
-    __syncthreads();
-    const int sl = s_slice;
-    if (sl < 0) {   // the weights sum to zero: the target row's argmax
+    const uint64_t *mb = mass + size_t(b) * ns;
+    __shared__ int s_slice, s_found;
+    __shared__ uint64_t s_rem;
+    // Total mass (exact), then t.
+    uint64_t part = 0;
+    for (int j = tid; j < ns; j += kThreads) part += mb[j];
+    uint64_t total;
+    block_excl_scan(part, &total);
+    if (total == 0) {   // every weight underflowed: the target row's argmax
         if (tid == 0) next[b] = pk.amax;
         return;
     }
+    uint64_t t = static_cast<uint64_t>(double(u_sample[b]) * double(total));
+    if (t >= total) t = total - 1;
+    if (tid == 0) s_slice = INT_MAX;
+    // The slice: chunks of kThreads slices, scanned in order.
+    uint64_t carry = 0;
+    for (int c0 = 0; c0 < ns; c0 += kThreads) {
+        const int j = c0 + tid;
+        const uint64_t mj = j < ns ? mb[j] : 0;
+        uint64_t csum;
+        const uint64_t ex = carry + block_excl_scan(mj, &csum);
+        if (j < ns && ex <= t && t < ex + mj) {   // exactly one slice owns t
+            s_slice = j;
+            s_rem = t - ex;
+        }
+        carry += csum;
+        __syncthreads();
+        if (s_slice != INT_MAX) break;
+    }
+    const int sl = s_slice;
+    const uint64_t rem = s_rem;
     // Within the slice: thread j owns entries lo + j kPer .. + kPer - 1, in order.
     const TIn *trow = tgt + (size_t(b) * T + pk.row) * V;
     const TIn *drow = pk.residual ? drf + (size_t(b) * (T - 1) + pk.row) * V : nullptr;
     const int lo = sl * kSlice + tid * kPer, hi = min(V, sl * kSlice + kSlice);
-    float w[kPer], mine = 0.f;
-    int lastpos = -1;
+    uint64_t w[kPer], mine = 0;
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
         const int i = lo + k;
-        w[k] = i < hi ? draw_weight(trow, drow, pk, inv_tau, i) : 0.f;
+        w[k] = i < hi ? draw_weight(trow, drow, pk, inv_tau, i) : 0;
         mine += w[k];
-        if (w[k] > 0.f) lastpos = i;
     }
-    tsum[tid] = mine;
+    uint64_t stot;
+    const uint64_t ex = block_excl_scan(mine, &stot);
+    // (The entries were weighed again here; should any weight come out
+    // differently from the mass kernel's, the target stays inside the slice.)
+    const uint64_t rm = stot > 0 && rem >= stot ? stot - 1 : rem;
+    if (tid == 0) s_found = INT_MAX;
     __syncthreads();
-    // Exclusive prefix of the thread sums (serial over the threads below: 256
-    // adds at most, in index order).
-    float excl = 0.f;
-    for (int j = 0; j < tid; ++j) excl += tsum[j];
-    // The owner is the thread whose share of the cumulative weight covers rem,
-    // tested with the same sums the next thread's prefix is made of; it takes
-    // its first entry whose running sum passes rem, or (rounding) its last entry
-    // with weight.
-    const float rem = s_rem;
-    if (excl <= rem && rem < excl + mine) {
-        float run = excl;
-        int pickd = lastpos;
+    if (ex <= rm && rm < ex + mine) {
+        uint64_t r = ex;
 #pragma unroll
         for (int k = 0; k < kPer; ++k) {
-            run += w[k];
-            if (run > rem && w[k] > 0.f) {
-                pickd = lo + k;
+            r += w[k];
+            if (r > rm) {
+                s_found = lo + k;
                 break;
             }
         }
-        atomicMin(&s_found, pickd);
     }
-    if (lastpos >= 0) atomicMax(&s_lastpos, lastpos);
     __syncthreads();
-    if (tid == 0) {
-        const int x = s_found != INT_MAX ? s_found : s_lastpos;
-        next[b] = x >= 0 ? x : pk.amax;
-    }
+    if (tid == 0) next[b] = s_found != INT_MAX ? s_found : pk.amax;
 }
 
 // Filter history rewind: thread per channel, the new window assembled in
@@ -358,7 +425,7 @@ AcceptWs accept_ws_layout(int B, int T, int V, bool sampled) {
     w.parts = 0;
     w.pick = w.parts + align256(size_t(B) * rows * ns * sizeof(Part));
     w.mass = w.pick + align256(size_t(B) * sizeof(Pick));
-    w.total = w.mass + (sampled ? align256(size_t(B) * ns * sizeof(float)) : 0);
+    w.total = w.mass + (sampled ? align256(size_t(B) * ns * sizeof(uint64_t)) : 0);
     return w;
 }
 
@@ -372,7 +439,7 @@ hipError_t accept_greedy_t(const TIn *tgt, const int32_t *drafts, int B, int T, 
                        static_cast<const TIn *>(nullptr), T, V, ns, 1.f, parts);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((accept_decide_kernel<TIn, false>), dim3(B), dim3(64), 0, st, tgt,
+    hipLaunchKernelGGL((accept_decide_kernel<TIn, false>), dim3(B), dim3(kThreads), 0, st, tgt,
                        static_cast<const TIn *>(nullptr), drafts, static_cast<const float *>(nullptr), T, V, ns,
                        1.f, parts, reinterpret_cast<Pick *>(ws + L.pick), n_out, next);
     return hipGetLastError();
@@ -386,12 +453,12 @@ hipError_t accept_sampled_t(const TIn *tgt, const TIn *drf, const int32_t *draft
     const AcceptWs L = accept_ws_layout(B, T, V, true);
     Part *parts = reinterpret_cast<Part *>(ws + L.parts);
     Pick *pick = reinterpret_cast<Pick *>(ws + L.pick);
-    float *mass = reinterpret_cast<float *>(ws + L.mass);
+    uint64_t *mass = reinterpret_cast<uint64_t *>(ws + L.mass);
     hipLaunchKernelGGL((accept_stats_kernel<TIn, true>), dim3(ns, 2 * T - 1, B), dim3(kThreads), 0, st, tgt, drf, T,
                        V, ns, inv_tau, parts);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((accept_decide_kernel<TIn, true>), dim3(B), dim3(64), 0, st, tgt, drf, drafts, u_acc, T, V,
+    hipLaunchKernelGGL((accept_decide_kernel<TIn, true>), dim3(B), dim3(kThreads), 0, st, tgt, drf, drafts, u_acc, T, V,
                        ns, inv_tau, parts, pick, n_out, static_cast<int32_t *>(nullptr));
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((accept_mass_kernel<TIn>), dim3(ns, B), dim3(kThreads), 0, st, tgt, drf, T, V, ns, inv_tau,
