@@ -464,8 +464,8 @@ def summarize_profiles(args):
 
     # Kernel-trace statistics.
     stats = _read_csv(os.path.join(d, "stats", "**", "*kernel_stats.csv"))
-    lines = ["# Kernel time: verify + commit (48 layers x 32 heads, d=128, T=8) and chunked "
-             "prefill (32 heads, L=4096)", "",
+    lines = ["# Kernel time: verify + commit (48 layers x 32 heads, d=128, T=8), chunked "
+             "prefill (32 heads, L=4096), plain decode (32 heads, T=1) and acceptance (T=8, V=151,936)", "",
              "rocprofv3 `--kernel-trace --stats` of the benchmark, GPU kernels of libgdn only "
              "(torch's input generation and copies omitted).", "", "Command:", "", "```",
              commands[0], "```", "", "| kernel | calls | average us | min us | max us | share of listed time |",
@@ -535,12 +535,14 @@ def summarize_profiles(args):
 
     # The fused kernel's dispatch i runs pass i (warmup, headline, kernel-timing
     # regions); the separate commits run passes warmup + 2 steps + i.
-    fus = kernel_rows("verify_kernel", ", true>")
+    # (Four tiles a wave: the 48-layer launches; the plain-decode leg's few-heads
+    # launches are not in the counter runs.)
+    fus = kernel_rows("verify_kernel", ", true, 4>")
     if fus:
         fus = fus[:total]
         summary["kernels"]["commit_verify_kernel"] = summarize(
             fus, [fused_bytes(LAYERS, HEADS, DK, DV, T, n_host[i], es) for i in range(len(fus))])
-    ver = kernel_rows("verify_kernel", ", false>")
+    ver = kernel_rows("verify_kernel", ", false, 4>")
     if ver:
         vb = verify_bytes(LAYERS, HEADS, DK, DV, T, es)
         fr = sum(r[1] for r in ver) / len(ver)
@@ -555,11 +557,12 @@ def summarize_profiles(args):
         com = com[:total - s2]
         summary["kernels"]["commit_kernel"] = summarize(
             com, [commit_bytes(LAYERS, HEADS, DK, DV, n_host[s2 + i], es) for i in range(len(com))])
-    # Prefill: every call launches either prefill_kernel or prep + scan; per call.
+    # Prefill: every call launches either prefill_kernel, or one prep launch and
+    # one stage launch per chunk segment; per call.
     pk = kernel_rows("prefill_kernel<")
     pp = kernel_rows("prefill_prep_kernel")
-    ps = kernel_rows("prefill_scan_kernel")
-    calls = len(ps) if ps else len(pk)
+    ps = kernel_rows("prefill_stage_kernel")
+    calls = len(pp) if pp else len(pk)
     if calls:
         fr = (sum(r[1] for r in pk + pp + ps)) / calls
         wr = (sum(r[2] for r in pk + pp + ps)) / calls
