@@ -16,3 +16,4 @@ from .gdn_oracle import (  # noqa: F401
     prefill_chunked,
 )
 from . import accept_oracle  # noqa: F401,E402  (acceptance and rewind, numpy fp64)
+from . import attn_oracle  # noqa: F401,E402  (full-attention verify, numpy fp64)
