@@ -315,6 +315,55 @@ int gdn_accept_sampled(const void *target_logits, const void *draft_logits, gdn_
 int gdn_history_rewind(void *history, const void *rows, const int32_t *n, int32_t B, int32_t W, int32_t T,
                        int32_t C, gdn_in_dtype dt, void *hip_stream);
 
+/* ---------------------------------------------------------------------------
+ * The full-attention mixer of the verify pass.
+ *
+ * Source: the README page ("How it works", region table): the full-attention
+ * mixer partitions the K/V context, accumulates online-softmax statistics
+ * locally and merges the partial results before the output projection; the
+ * audited-numbers page ("How does lithos-metal fuse layer mixers on Metal?"): 16
+ * of the 64 layers are full attention, and workers keep small running softmax
+ * totals in fp32 so the full score table is never written.
+ * ------------------------------------------------------------------------- */
+
+/* B instances (layers x sequences), Hq query heads, Hkv key/value heads (Hq a
+ * multiple of Hkv; query head h reads key/value head h / (Hq / Hkv)), head size
+ * d in {128, 256}, cache capacity Lmax positions. */
+typedef struct {
+    int32_t B, Hq, Hkv, d, Lmax;
+} gdn_attn_shape;
+
+/* Workspace bytes of gdn_attn_verify for blocks of T rows (the split partials:
+ * per query row and split, a running max, a sum and d accumulators, fp32); 0
+ * for an invalid shape. */
+size_t gdn_attn_workspace_bytes(const gdn_attn_shape *shp, int32_t T);
+
+/*
+ * Attention of a T-row verify block.  Query row (t, h) attends to cache
+ * positions 0 .. ctx[b]-1 and to the block's rows 0 .. t:
+ *   o[b][t][h] = sum_p softmax_p(scale * q[b][t][h] . key_p) value_p.
+ * The block's key/value rows are also written into the cache at positions
+ * ctx[b] .. ctx[b]+T-1; rewinding the cache is then setting its length (the
+ * position gdn_commit advances by n).
+ *
+ *   q        bf16 [B][T][Hq][d];  k_new, v_new  bf16 [B][T][Hkv][d]: the block's
+ *            keys and values.
+ *   k_cache, v_cache   bf16 [B][Lmax][Hkv][d], in/out (rows ctx .. ctx+T-1
+ *            written).
+ *   ctx      int32 [B] on the device: cached positions, 0 <= ctx <= Lmax - T; an
+ *            instance outside that range gets NaN outputs and no cache write.
+ *   scale    the score scale (1/sqrt(d) in the usual form), finite.
+ *   o        fp32 [B][T][Hq][d], written.
+ *   ws       device workspace of gdn_attn_workspace_bytes(shp, T) bytes, 16-byte
+ *            aligned; contents are scratch.
+ * Constraints: 1 <= T <= GDN_T_MAX, T * (Hq / Hkv) <= 256, Lmax >= T.  Returns
+ * GDN_OK, or before any launch GDN_EINVAL (null or misaligned pointer), GDN_EDIM
+ * (shape), GDN_ERANGE (T, scale), GDN_EWS, or GDN_EHIP.
+ */
+int gdn_attn_verify(const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                    const int32_t *ctx, int32_t T, float scale, const gdn_attn_shape *shp, float *o, void *ws,
+                    size_t ws_bytes, void *hip_stream);
+
 /* Static description of a gdn_status value; never NULL. */
 const char *gdn_strerror(int status);
 

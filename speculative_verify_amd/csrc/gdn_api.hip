@@ -37,6 +37,16 @@ int check_accept_shape(const gdn_accept_shape *s) {
     return GDN_OK;
 }
 
+int check_attn_shape(const gdn_attn_shape *s, int32_t T) {
+    if (s == nullptr) return GDN_EINVAL;
+    if (s->B < 1 || s->B > 65535 || s->Hkv < 1 || s->Hq < s->Hkv || s->Hq % s->Hkv != 0) return GDN_EDIM;
+    if (s->d != 128 && s->d != 256) return GDN_EDIM;
+    if (T < 1 || T > GDN_T_MAX) return GDN_ERANGE;
+    if (s->Lmax < T || int64_t(T) * (s->Hq / s->Hkv) > 256) return GDN_EDIM;
+    if (int64_t(s->B) * s->Lmax * s->Hkv * s->d > (int64_t(1) << 40)) return GDN_EDIM;
+    return GDN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -181,6 +191,25 @@ int gdn_history_rewind(void *history, const void *rows, const int32_t *n, int32_
     if (!aligned(history, es) || !aligned(rows, es) || !aligned(n, 4)) return GDN_EINVAL;
     return hip_status(
         launch_history_rewind(history, rows, n, B, W, T, C, dt, static_cast<hipStream_t>(hip_stream)));
+}
+
+size_t gdn_attn_workspace_bytes(const gdn_attn_shape *shp, int32_t T) {
+    if (check_attn_shape(shp, T) != GDN_OK) return 0;
+    return attn_workspace_bytes(*shp, T);
+}
+
+int gdn_attn_verify(const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                    const int32_t *ctx, int32_t T, float scale, const gdn_attn_shape *shp, float *o, void *ws,
+                    size_t ws_bytes, void *hip_stream) {
+    int rc = check_attn_shape(shp, T);
+    if (rc != GDN_OK) return rc;
+    if (!std::isfinite(scale)) return GDN_ERANGE;
+    if (!aligned(q, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) ||
+        !aligned(v_cache, 16) || !aligned(ctx, 4) || !aligned(o, 16) || !aligned(ws, 16))
+        return GDN_EINVAL;
+    if (ws_bytes < attn_workspace_bytes(*shp, T)) return GDN_EWS;
+    return hip_status(launch_attn_verify(q, k_new, v_new, k_cache, v_cache, ctx, T, scale, *shp, o, ws,
+                                         static_cast<hipStream_t>(hip_stream)));
 }
 
 const char *gdn_strerror(int status) {

@@ -196,6 +196,10 @@ hipError_t launch_prefill(float *S, const void *q, const void *k, const void *v,
 // length (0 when the one-pass schedule is the faster one).
 size_t prefill_workspace_bytes(const gdn_shape &shp, int L);
 size_t accept_workspace_bytes(int B, int T, int V, bool sampled);
+size_t attn_workspace_bytes(const gdn_attn_shape &s, int T);
+hipError_t launch_attn_verify(const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                              const int32_t *ctx, int T, float scale, const gdn_attn_shape &s, float *o, void *ws,
+                              hipStream_t st);
 hipError_t launch_accept_greedy(const void *tgt, gdn_in_dtype dt, const int32_t *drafts, int B, int T, int V,
                                 int32_t *n_out, int32_t *next, void *ws, hipStream_t st);
 hipError_t launch_accept_sampled(const void *tgt, const void *drf, gdn_in_dtype dt, const int32_t *drafts,

@@ -36,6 +36,8 @@ EXPORTED = (
     "gdn_accept_greedy",
     "gdn_accept_sampled",
     "gdn_history_rewind",
+    "gdn_attn_workspace_bytes",
+    "gdn_attn_verify",
     "gdn_strerror",
 )
 GDN_HISTORY_MAX = 16
@@ -54,6 +56,11 @@ class gdn_shape(ctypes.Structure):
 
 class gdn_accept_shape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("V", ctypes.c_int32)]
+
+
+class gdn_attn_shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("Lmax", ctypes.c_int32)]
 
 
 def _load() -> ctypes.CDLL:
@@ -85,6 +92,11 @@ def _load() -> ctypes.CDLL:
     lib.gdn_accept_sampled.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp, ctypes.c_float, ap, vp, vp, vp, sz, vp]
     lib.gdn_history_rewind.restype = ctypes.c_int
     lib.gdn_history_rewind.argtypes = [vp, vp, vp, i32, i32, i32, i32, ctypes.c_int, vp]
+    tp = ctypes.POINTER(gdn_attn_shape)
+    lib.gdn_attn_workspace_bytes.restype = sz
+    lib.gdn_attn_workspace_bytes.argtypes = [tp, i32]
+    lib.gdn_attn_verify.restype = ctypes.c_int
+    lib.gdn_attn_verify.argtypes = [vp] * 6 + [i32, ctypes.c_float, tp, vp, vp, sz, vp]
     lib.gdn_strerror.restype = ctypes.c_char_p
     lib.gdn_strerror.argtypes = [ctypes.c_int]
     return lib
@@ -315,3 +327,47 @@ def gdn_history_rewind(history, rows, n, stream=None) -> None:
                                 _stream(stream))
     if rc != 0:
         raise GdnError(rc, "gdn_history_rewind")
+
+
+def _attn_shape(q, k_cache) -> gdn_attn_shape:
+    if q.dim() != 4 or k_cache.dim() != 4:
+        raise ValueError("q must be [B][T][Hq][d] and k_cache [B][Lmax][Hkv][d]")
+    B, T, Hq, d = q.shape
+    _, Lmax, Hkv, dk = k_cache.shape
+    if dk != d or k_cache.shape[0] != B:
+        raise ValueError("k_cache must be [B][Lmax][Hkv][d] with q's B and d")
+    return gdn_attn_shape(B, Hq, Hkv, d, Lmax)
+
+
+def gdn_attn_workspace_bytes(q, k_cache) -> int:
+    return int(lib.gdn_attn_workspace_bytes(ctypes.byref(_attn_shape(q, k_cache)), q.shape[1]))
+
+
+def gdn_attn_verify(q, k_new, v_new, k_cache, v_cache, ctx, o, scale=None, ws=None, stream=None) -> None:
+    """Attention of a verify block (see gdn_attn_verify in include/gdn.h): o[:] =
+    outputs, the block's keys and values written into the caches at ctx .. ctx+T-1.
+    ``scale`` defaults to 1/sqrt(d); ``ws`` is the workspace of
+    gdn_attn_workspace_bytes bytes (allocated here when None, device memory only)."""
+    shp = _attn_shape(q, k_cache)
+    B, T, Hq, d = q.shape
+    want = {"k_new": (k_new, (B, T, shp.Hkv, d)), "v_new": (v_new, (B, T, shp.Hkv, d)),
+            "v_cache": (v_cache, tuple(k_cache.shape))}
+    for name, (x, shape) in want.items():
+        if tuple(x.shape) != shape or x.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be bf16 {shape}")
+    if q.dtype != torch.bfloat16 or k_cache.dtype != torch.bfloat16:
+        raise ValueError("q and the caches must be bf16")
+    if tuple(ctx.shape) != (B,) or ctx.dtype != torch.int32:
+        raise ValueError("ctx must be int32 [B]")
+    if tuple(o.shape) != (B, T, Hq, d) or o.dtype != torch.float32:
+        raise ValueError("o must be float32 [B][T][Hq][d]")
+    if scale is None:
+        scale = 1.0 / float(d) ** 0.5
+    if ws is None:
+        need = int(lib.gdn_attn_workspace_bytes(ctypes.byref(shp), T))
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    nb = ws.numel() * ws.element_size()
+    rc = lib.gdn_attn_verify(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(ctx), T,
+                             float(scale), ctypes.byref(shp), _ptr(o), _ptr(ws), nb, _stream(stream))
+    if rc != 0:
+        raise GdnError(rc, "gdn_attn_verify")

@@ -155,3 +155,36 @@ def make_history_inputs(B: int, W: int, T: int, C: int, *, dtype=torch.bfloat16,
     hist = torch.randn(B, W, C, generator=gen).to(dtype)
     rows = torch.randn(B, T, C, generator=gen).to(dtype)
     return hist.to(device), rows.to(device)
+
+
+# ---------------------------------------------------------------------------
+# Full-attention inputs: one verify block's queries, its new keys and values,
+# and a key/value cache, all N(0,1) rounded to bf16 (cache rows past ctx hold
+# N(0,1) too: they must not be read).  Draw order: q, k_new, v_new, k_cache,
+# v_cache.  Drawn on the CPU generator, or on the device with device_gen.
+# ---------------------------------------------------------------------------
+@dataclass
+class AttnInputs:
+    q: torch.Tensor        # bf16 [B][T][Hq][d]
+    k_new: torch.Tensor    # bf16 [B][T][Hkv][d]
+    v_new: torch.Tensor
+    k_cache: torch.Tensor  # bf16 [B][Lmax][Hkv][d]
+    v_cache: torch.Tensor
+    ctx: torch.Tensor      # int32 [B]
+
+    def to(self, device) -> "AttnInputs":
+        return AttnInputs(*(getattr(self, f).to(device) for f in ("q", "k_new", "v_new", "k_cache", "v_cache", "ctx")))
+
+
+def make_attn_inputs(B: int, T: int, Hq: int, Hkv: int, d: int, Lmax: int, ctx, *, seed: int = 0, device="cpu",
+                     device_gen: bool = False) -> AttnInputs:
+    gen_dev = torch.device(device) if device_gen else torch.device("cpu")
+    gen = torch.Generator(device=gen_dev)
+    gen.manual_seed(int(seed) + 15485863)
+
+    def randn(*shape):
+        return torch.randn(*shape, generator=gen, device=gen_dev, dtype=torch.float32).to(torch.bfloat16)
+
+    out = AttnInputs(randn(B, T, Hq, d), randn(B, T, Hkv, d), randn(B, T, Hkv, d), randn(B, Lmax, Hkv, d),
+                     randn(B, Lmax, Hkv, d), torch.as_tensor(ctx, dtype=torch.int32).reshape(B).to(gen_dev))
+    return out.to(device) if gen_dev != torch.device(device) else out

@@ -173,3 +173,27 @@ def test_accept_and_rewind_reject_bad_arguments(G):
     assert rewind(W=0) == -3
     assert rewind(W=17) == -3
     assert rewind(T=17) == -3
+
+
+def test_attn_rejects_bad_arguments(G):
+    L = G.lib
+
+    def shp(B=1, Hq=16, Hkv=2, d=256, Lmax=1024):
+        return ctypes.byref(G.gdn_attn_shape(B, Hq, Hkv, d, Lmax))
+
+    def call(T=8, scale=0.0625, s=None, q=FAKE, ws=FAKE, wsb=1 << 40):
+        return L.gdn_attn_verify(q, FAKE, FAKE, FAKE, FAKE, FAKE, T, scale, s or shp(), FAKE, ws, wsb, None)
+
+    assert call(q=None) == -1
+    assert call(ws=FAKE_ODD) == -1
+    assert call(s=shp(d=64)) == -2
+    assert call(s=shp(Hq=3, Hkv=2)) == -2
+    assert call(s=shp(Hkv=0)) == -2
+    assert call(s=shp(Lmax=4)) == -2
+    assert call(s=shp(Hq=64, Hkv=2), T=16) == -2     # 16 x 32 query rows per key/value head
+    assert call(T=0) == -3
+    assert call(T=17) == -3
+    assert call(scale=float("inf")) == -3
+    assert call(wsb=16) == -4
+    assert L.gdn_attn_workspace_bytes(shp(), 8) > 0
+    assert L.gdn_attn_workspace_bytes(shp(d=64), 8) == 0
