@@ -49,6 +49,7 @@ def parse():
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-accept", action="store_true")
+    p.add_argument("--no-attn", action="store_true")
     p.add_argument("--decode-steps", type=int, default=10000)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget-s", type=float, default=15.0)
@@ -401,6 +402,8 @@ def main():
         result["decode"] = bench_decode(args, G, dev)
     if not args.no_accept:
         result["accept"] = bench_accept(args, G, dev)
+    if not args.no_attn:
+        result["attn"] = bench_attn(args, G, dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args)
     if args.copy_calibration_mib > 0:
@@ -711,6 +714,51 @@ def bench_accept(args, G, dev):
         out[name] = {"us_per_call_eager": round(eager, 2), "us_per_call_graph": round(gus, 2),
                      "algorithmic_bytes": nbytes[name],
                      "effective_GBs_graph": round(nbytes[name] / (gus * 1e-6) / 1e9, 1)}
+    return out
+
+
+ATT_LAYERS, ATT_HQ, ATT_HKV, ATT_D = 16, 16, 2, 256   # the 16 full-attention layers (Qwen3-Next-style heads)
+
+
+def attn_bytes(B, T, Hq, Hkv, d, ctx):
+    """Algorithmic HBM bytes of one attention call: the cached keys and values
+    read once, the block's queries, keys and values read, the outputs written
+    and the block's rows appended to the cache."""
+    return (B * ctx * Hkv * d * 2 * 2 + B * T * (Hq + 2 * Hkv) * d * 2 + B * T * Hq * d * 4
+            + B * T * Hkv * d * 2 * 2)
+
+
+def bench_attn(args, G, dev):
+    """The verify pass's 16 full-attention layers (16 query / 2 key-value heads,
+    d = 256, bf16 cache), T = 8, at 32,760 and at 120 cached positions; timed
+    over 20 calls with events, caches flushed by the 1 GiB working set itself."""
+    import torch
+
+    from speculative_verify_amd.inputs import make_attn_inputs
+
+    B, Tb, Lmax = ATT_LAYERS, T, 32768
+    out = {"workload": f"full-attention verify: {B} layers x {ATT_HQ} query / {ATT_HKV} key-value heads, "
+                       f"d={ATT_D}, T={Tb}, bf16 K/V cache of {Lmax} positions"}
+    x = make_attn_inputs(B, Tb, ATT_HQ, ATT_HKV, ATT_D, Lmax, [Lmax - Tb] * B, seed=args.seed + 33, device=dev,
+                         device_gen=True)
+    o = torch.empty(B, Tb, ATT_HQ, ATT_D, dtype=torch.float32, device=dev)
+    ws = torch.empty(G.gdn_attn_workspace_bytes(x.q, x.k_cache), dtype=torch.uint8, device=dev)
+    for name, ctx in (("ctx_32760", Lmax - Tb), ("ctx_120", 120)):
+        c = torch.full((B,), ctx, dtype=torch.int32, device=dev)
+        G.gdn_attn_verify(x.q, x.k_new, x.v_new, x.k_cache, x.v_cache, c, o, ws=ws)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n = 20
+        a.record()
+        for _ in range(n):
+            G.gdn_attn_verify(x.q, x.k_new, x.v_new, x.k_cache, x.v_cache, c, o, ws=ws)
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) / n * 1e3
+        nb = attn_bytes(B, Tb, ATT_HQ, ATT_HKV, ATT_D, ctx)
+        gbs = nb / (us * 1e-6) / 1e9
+        out[name] = {"us_per_call": round(us, 2), "algorithmic_bytes": nb, "achieved_GBs": round(gbs, 1),
+                     "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "workspace_bytes": ws.numel()}
     return out
 
 

@@ -243,57 +243,65 @@ __global__ __launch_bounds__(256) void attn_split_kernel(
     }
 }
 
-// Merge: one workgroup per (instance, key/value head, 64 query rows); thread
-// (row, 16-element run) combines the splits: o = sum_s 2^(m_s - M) acc_s /
-// sum_s 2^(m_s - M) l_s.  An instance whose ctx is out of range gets NaN.
+// Merge: thread (query row, 4 consecutive d) of one (instance, key/value head,
+// 64 query rows) combines the splits: o = sum_s 2^(m_s - M) acc_s / sum_s
+// 2^(m_s - M) l_s.  kMergeWg workgroups cover the 64 x D / 4 items of a row
+// group.  An instance whose ctx is out of range gets NaN.
+constexpr int kMergeChunk = 8;   // splits whose loads are issued together
+
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(const float *__restrict__ part_acc,
                                                          const float *__restrict__ part_ml,
                                                          const int32_t *__restrict__ ctx_arr, int T, int Hq,
                                                          int Hkv, int Lmax, int nspl, float *__restrict__ o) {
-    const int gy = blockIdx.x, b = blockIdx.y;
+    constexpr int RUNS = D / 4;                       // float4 runs of a row
+    constexpr int WGS = kRows * RUNS / 256;           // workgroups per row group
+    const int gy = blockIdx.x / WGS, part = blockIdx.x - gy * WGS, b = blockIdx.y;
     const int G = Hq / Hkv, R = T * G, RG = (R + kRows - 1) / kRows;
     const int g = gy / RG, rg = gy - g * RG;
+    const int e = part * 256 + threadIdx.x;
+    const int row = e / RUNS, d0 = (e - row * RUNS) * 4;
+    const int qi = rg * kRows + row;
+    if (qi >= R) return;
+    const int t = qi / G, h = g * G + qi % G;
+    float4 *dst = reinterpret_cast<float4 *>(o + ((size_t(b) * T + t) * Hq + h) * D + d0);
     const int ctx = ctx_arr[b];
-    const bool bad = ctx < 0 || ctx > Lmax - T;
-    constexpr int RUNS = D / 16;
-    for (int e = threadIdx.x; e < kRows * RUNS; e += 256) {
-        const int row = e / RUNS, d0 = (e - row * RUNS) * 16;
-        const int qi = rg * kRows + row;
-        if (qi >= R) continue;
-        const int t = qi / G, h = g * G + qi % G;
-        float *dst = o + ((size_t(b) * T + t) * Hq + h) * D + d0;
-        if (bad) {
-            for (int i = 0; i < 16; ++i) dst[i] = __builtin_nanf("");
-            continue;
-        }
-        const size_t base = ((size_t(b) * Hkv + g) * RG + rg) * nspl;
-        float M = -INFINITY;
-        for (int s = 0; s < nspl; ++s) M = fmaxf(M, part_ml[((base + s) * kRows + row) * 2]);
-        float L = 0.f, acc[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-        for (int s = 0; s < nspl; ++s) {
-            const float ms = part_ml[((base + s) * kRows + row) * 2];
-            if (ms == -INFINITY) continue;
-            const float f = exp2f(ms - M);
-            L += f * part_ml[((base + s) * kRows + row) * 2 + 1];
-            const float4 *pa = reinterpret_cast<const float4 *>(part_acc + ((base + s) * kRows + row) * D + d0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float4 v = pa[i];
-                acc[4 * i] += f * v.x;
-                acc[4 * i + 1] += f * v.y;
-                acc[4 * i + 2] += f * v.z;
-                acc[4 * i + 3] += f * v.w;
-            }
-        }
-        const float inv = 1.f / L;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            reinterpret_cast<float4 *>(dst)[i] =
-                make_float4(acc[4 * i] * inv, acc[4 * i + 1] * inv, acc[4 * i + 2] * inv, acc[4 * i + 3] * inv);
+    if (ctx < 0 || ctx > Lmax - T) {
+        const float nan = __builtin_nanf("");
+        *dst = make_float4(nan, nan, nan, nan);
+        return;
     }
+    const size_t base = ((size_t(b) * Hkv + g) * RG + rg) * nspl;
+    const float *ml = part_ml + (base * kRows + row) * 2;   // split s at ml[s * 2 * kRows]
+    const float *pa = part_acc + (base * kRows + row) * D + d0;
+    float M = -INFINITY;
+    for (int s = 0; s < nspl; ++s) M = fmaxf(M, ml[size_t(s) * 2 * kRows]);
+    float L = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s0 = 0; s0 < nspl; s0 += kMergeChunk) {
+        float m[kMergeChunk], l[kMergeChunk];
+        float4 a[kMergeChunk];
+#pragma unroll
+        for (int k = 0; k < kMergeChunk; ++k) {
+            const int s = s0 + k;
+            m[k] = s < nspl ? ml[size_t(s) * 2 * kRows] : -INFINITY;
+            l[k] = s < nspl ? ml[size_t(s) * 2 * kRows + 1] : 0.f;
+            a[k] = s < nspl ? *reinterpret_cast<const float4 *>(pa + size_t(s) * kRows * D)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int k = 0; k < kMergeChunk; ++k) {
+            if (m[k] == -INFINITY) continue;
+            const float f = exp2f(m[k] - M);
+            L += f * l[k];
+            acc.x += f * a[k].x;
+            acc.y += f * a[k].y;
+            acc.z += f * a[k].z;
+            acc.w += f * a[k].w;
+        }
+    }
+    const float inv = 1.f / L;
+    *dst = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
 }
 
 int split_count(int B, int Hkv, int RG, int Lmax, int T) {
@@ -325,8 +333,8 @@ hipError_t attn_t(const void *q, const void *k_new, const void *v_new, void *k_c
                        part_acc, part_ml);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_merge_kernel<D>), dim3(s.Hkv * RG, s.B), dim3(256), 0, st, part_acc, part_ml, ctx, T,
-                       s.Hq, s.Hkv, s.Lmax, nspl, o);
+    hipLaunchKernelGGL((attn_merge_kernel<D>), dim3(s.Hkv * RG * (kRows * D / 4 / 256), s.B), dim3(256), 0, st,
+                       part_acc, part_ml, ctx, T, s.Hq, s.Hkv, s.Lmax, nspl, o);
     return hipGetLastError();
 }
 
