@@ -17,3 +17,4 @@ from .gdn_oracle import (  # noqa: F401
 )
 from . import accept_oracle  # noqa: F401,E402  (acceptance and rewind, numpy fp64)
 from . import attn_oracle  # noqa: F401,E402  (full-attention verify, numpy fp64)
+from . import mixer_oracle  # noqa: F401,E402  (GDN mixer prologue/epilogue, numpy fp64)
