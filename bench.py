@@ -50,6 +50,7 @@ def parse():
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-accept", action="store_true")
     p.add_argument("--no-attn", action="store_true")
+    p.add_argument("--no-mixer", action="store_true")
     p.add_argument("--decode-steps", type=int, default=10000)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget-s", type=float, default=15.0)
@@ -404,6 +405,8 @@ def main():
         result["accept"] = bench_accept(args, G, dev)
     if not args.no_attn:
         result["attn"] = bench_attn(args, G, dev)
+    if not args.no_mixer:
+        result["mixer"] = bench_mixer(args, G, dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args)
     if args.copy_calibration_mib > 0:
@@ -718,6 +721,48 @@ def bench_accept(args, G, dev):
 
 
 ATT_LAYERS, ATT_HQ, ATT_HKV, ATT_D = 16, 16, 2, 256   # the 16 full-attention layers (Qwen3-Next-style heads)
+MIX_HK = 16   # q/k heads of the GDN mixer (value heads: HEADS)
+
+
+def bench_mixer(args, G, dev):
+    """The 48-layer pass with the GDN mixer fused around the recurrence: one
+    gdn_mixer_commit_verify per pass (filter, norms and gates from the raw
+    in-projection rows; gated RMS norm on the outputs) against one
+    gdn_commit_verify on ready q, k, v, at the same accepted lengths."""
+    import torch
+
+    from speculative_verify_amd.inputs import make_accepts, make_inputs, make_mixer_inputs
+
+    L, H = LAYERS, HEADS
+    x = make_inputs(L, H, DK, DV, T, seed=args.seed + 61, device=dev, device_gen=True)
+    m = make_mixer_inputs(L, T, H, MIX_HK, DK, seed=args.seed + 61, device=dev)
+    ns = make_accepts(64, T, seed=args.seed + 61)
+    nt = [torch.full((L,), int(v), dtype=torch.int32, device=dev) for v in ns]
+    y = torch.empty(L, T, H, DV, dtype=torch.float32, device=dev)
+    S = x.S0.clone()
+    recs = [G.new_record(S, T, torch.bfloat16) for _ in range(2)]
+    out = {"workload": f"{L} GDN layers x {H} value heads ({MIX_HK} q/k heads), d={DK}, T={T}: commit + verify "
+                       f"per pass, n~U{{0..8}}"}
+    for name in ("mixer_commit_verify", "commit_verify"):
+        if name == "mixer_commit_verify":
+            G.gdn_mixer_verify(S, m, y, recs[0])
+            step = lambda i: G.gdn_mixer_commit_verify(S, recs[i % 2], nt[i % len(nt)], m, y, recs[(i + 1) % 2])
+        else:
+            G.gdn_verify_block(S, x.q, x.k, x.v, x.g, x.beta, y, recs[0])
+            step = lambda i: G.gdn_commit_verify(S, recs[i % 2], nt[i % len(nt)], x.q, x.k, x.v, x.g, x.beta, y,
+                                                 recs[(i + 1) % 2])
+        for i in range(10):
+            step(i)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n = 100
+        a.record()
+        for i in range(10, 10 + n):
+            step(i)
+        b.record()
+        torch.cuda.synchronize()
+        out[name + "_us"] = round(a.elapsed_time(b) / n * 1e3, 2)
+    return out
 
 
 def attn_bytes(B, T, Hq, Hkv, d, ctx):

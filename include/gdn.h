@@ -316,6 +316,62 @@ int gdn_history_rewind(void *history, const void *rows, const int32_t *n, int32_
                        int32_t C, gdn_in_dtype dt, void *hip_stream);
 
 /* ---------------------------------------------------------------------------
+ * The GDN mixer around the recurrence, fused into the verify.
+ *
+ * Source: the README page ("How it works", region table, "GDN mixer" row): the
+ * mixer's megakernel coordinates projections, recurrence, gating and
+ * normalisation through their dependencies; the audited-numbers page (DSpark
+ * section): a small filter layer keeps a short history of its inputs.  The pages
+ * give no formulas; these follow the published Gated DeltaNet layer (ICLR 2025)
+ * as deployed in the Qwen3-Next hybrid.  Per token, from the layer's raw
+ * in-projection row x (conv_dim = 2 Hk dk + H dv channels: q heads | k heads |
+ * v heads):
+ *   c = SiLU(sum_j w[c][j] x_{t-3+j}[c])      width-4 causal filter over the
+ *                                             3-row history and the block
+ *   q = c_q / |c_q| / sqrt(dk), k = c_k / |c_k|   per q/k head (eps 1e-6 under
+ *                                             the root); value head h reads q/k
+ *                                             head h / (H / Hk)
+ *   v = c_v;  q, k, v rounded to bf16
+ *   beta = sigmoid(b), g = -exp(A_log) softplus(a + dt_bias)
+ * then the verify (or commit + verify) of gdn_verify_block / gdn_commit_verify,
+ * and per token and value head
+ *   y = o / sqrt(mean(o^2) + 1e-6) * norm_w * SiLU(z).
+ * The block record holds the normalised keys, so gdn_commit and
+ * gdn_commit_verify consume it as any other; gdn_history_rewind updates the
+ * filter history with the rows x and the accepted n.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+    const void *x;           /* bf16 [B][T][conv_dim]: raw in-projection rows of the block */
+    const void *history;     /* bf16 [B][3][conv_dim]: the filter's last 3 inputs, oldest first */
+    const float *conv_w;     /* fp32 [conv_dim][4]: filter taps, tap 3 on the current row */
+    const float *a, *b;      /* fp32 [B][T][H]: decay and beta pre-activations */
+    const float *A_log;      /* fp32 [H] */
+    const float *dt_bias;    /* fp32 [H] */
+    const void *z;           /* bf16 [B][T][H][dv]: output gate pre-activation */
+    const float *norm_w;     /* fp32 [dv]: RMS-norm weight */
+    int32_t Hk;              /* q/k heads, H a multiple of Hk */
+} gdn_mixer_inputs;
+
+/*
+ * gdn_verify_block with the mixer: S fp32 [B][H][128][128] (read only), inputs
+ * as above, 1 <= T <= GDN_T_MAX, shp with dk = dv = 128; y fp32 [B][T][H][128]
+ * (the gated, normalised outputs); record as for gdn_verify_block with bf16
+ * inputs.  All pointers device memory owned by the caller, 16-byte aligned
+ * (4-byte for the fp32 vectors).  Returns GDN_OK, or before any launch
+ * GDN_EINVAL, GDN_EDIM (not dk = dv = 128, or H not a multiple of Hk),
+ * GDN_ERANGE (T), GDN_EWS (record too small), GDN_EHIP.
+ */
+int gdn_mixer_verify(const float *S, const gdn_mixer_inputs *in, int32_t T, const gdn_shape *shp, float *y,
+                     void *record, size_t record_bytes, void *hip_stream);
+
+/* gdn_commit_verify with the mixer: commit record_prev at n_accepted[b] rows,
+ * then the mixer verify of the next block into record_next (errors and device
+ * behaviour as for gdn_commit_verify and gdn_mixer_verify). */
+int gdn_mixer_commit_verify(float *S, void *record_prev, const int32_t *n_accepted, int32_t *pos,
+                            const gdn_mixer_inputs *in, int32_t T, const gdn_shape *shp, float *y,
+                            void *record_next, size_t record_next_bytes, void *hip_stream);
+
+/* ---------------------------------------------------------------------------
  * The full-attention mixer of the verify pass.
  *
  * Source: the README page ("How it works", region table): the full-attention

@@ -37,6 +37,21 @@ int check_accept_shape(const gdn_accept_shape *s) {
     return GDN_OK;
 }
 
+// The mixer's inputs and shape: d = 128, H a multiple of Hk, every pointer set
+// and aligned.
+int check_mixer(const gdn_mixer_inputs *in, const gdn_shape *shp, int32_t T) {
+    int rc = check_shape(shp);
+    if (rc != GDN_OK) return rc;
+    if (in == nullptr) return GDN_EINVAL;
+    if (shp->dk != 128 || shp->dv != 128 || in->Hk < 1 || shp->H % in->Hk != 0) return GDN_EDIM;
+    if (T < 1 || T > GDN_T_MAX) return GDN_ERANGE;
+    if (!aligned(in->x, 16) || !aligned(in->history, 16) || !aligned(in->conv_w, 16) || !aligned(in->a, 4) ||
+        !aligned(in->b, 4) || !aligned(in->A_log, 4) || !aligned(in->dt_bias, 4) || !aligned(in->z, 2) ||
+        !aligned(in->norm_w, 4))
+        return GDN_EINVAL;
+    return GDN_OK;
+}
+
 int check_attn_shape(const gdn_attn_shape *s, int32_t T) {
     if (s == nullptr) return GDN_EINVAL;
     if (s->B < 1 || s->B > 65535 || s->Hkv < 1 || s->Hq < s->Hkv || s->Hq % s->Hkv != 0) return GDN_EDIM;
@@ -191,6 +206,32 @@ int gdn_history_rewind(void *history, const void *rows, const int32_t *n, int32_
     if (!aligned(history, es) || !aligned(rows, es) || !aligned(n, 4)) return GDN_EINVAL;
     return hip_status(
         launch_history_rewind(history, rows, n, B, W, T, C, dt, static_cast<hipStream_t>(hip_stream)));
+}
+
+int gdn_mixer_verify(const float *S, const gdn_mixer_inputs *in, int32_t T, const gdn_shape *shp, float *y,
+                     void *record, size_t record_bytes, void *hip_stream) {
+    int rc = check_mixer(in, shp, T);
+    if (rc != GDN_OK) return rc;
+    if (!aligned(S, 16) || !aligned(y, 16) || !aligned(record, 16)) return GDN_EINVAL;
+    if (record_bytes < gdn_block_record_bytes(shp, T, GDN_IN_BF16)) return GDN_EWS;
+    return hip_status(launch_mixer_verify(S, *in, T, *shp, y, record, static_cast<hipStream_t>(hip_stream)));
+}
+
+int gdn_mixer_commit_verify(float *S, void *record_prev, const int32_t *n_accepted, int32_t *pos,
+                            const gdn_mixer_inputs *in, int32_t T, const gdn_shape *shp, float *y,
+                            void *record_next, size_t record_next_bytes, void *hip_stream) {
+    int rc = check_mixer(in, shp, T);
+    if (rc != GDN_OK) return rc;
+    if (!aligned(S, 16) || !aligned(y, 16) || !aligned(record_prev, 16) || !aligned(record_next, 16) ||
+        !aligned(n_accepted, 4))
+        return GDN_EINVAL;
+    if (pos != nullptr && !aligned(pos, 4)) return GDN_EINVAL;
+    const uintptr_t rp = reinterpret_cast<uintptr_t>(record_prev), rn = reinterpret_cast<uintptr_t>(record_next);
+    if (rp >= rn && rp < rn + record_next_bytes) return GDN_EINVAL;
+    if (rn > rp && rn - rp < 256) return GDN_EINVAL;
+    if (record_next_bytes < gdn_block_record_bytes(shp, T, GDN_IN_BF16)) return GDN_EWS;
+    return hip_status(launch_mixer_commit_verify(S, record_prev, n_accepted, pos, *in, T, *shp, y, record_next,
+                                                 static_cast<hipStream_t>(hip_stream)));
 }
 
 size_t gdn_attn_workspace_bytes(const gdn_attn_shape *shp, int32_t T) {

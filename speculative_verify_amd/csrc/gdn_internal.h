@@ -197,6 +197,11 @@ hipError_t launch_prefill(float *S, const void *q, const void *k, const void *v,
 size_t prefill_workspace_bytes(const gdn_shape &shp, int L);
 size_t accept_workspace_bytes(int B, int T, int V, bool sampled);
 size_t attn_workspace_bytes(const gdn_attn_shape &s, int T);
+hipError_t launch_mixer_verify(const float *S, const gdn_mixer_inputs &in, int T, const gdn_shape &shp, float *y,
+                               void *record, hipStream_t stream);
+hipError_t launch_mixer_commit_verify(float *S, void *record_prev, const int32_t *n_accepted, int32_t *pos,
+                                      const gdn_mixer_inputs &in, int T, const gdn_shape &shp, float *y,
+                                      void *record_next, hipStream_t stream);
 hipError_t launch_attn_verify(const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,
                               const int32_t *ctx, int T, float scale, const gdn_attn_shape &s, float *o, void *ws,
                               hipStream_t st);

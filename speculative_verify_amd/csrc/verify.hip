@@ -64,6 +64,50 @@ __device__ inline bf16x8 xrow_bf16(const uint8_t *Xb, int x, int p, int lg) {
     return __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// The GDN mixer around the recurrence (MIX): the kernel builds q, k, v and the
+// gates itself from the layer's raw in-projection rows, and applies the gated
+// RMS norm to its outputs.  Per token: a width-4 causal filter over the filter
+// history and the block (per channel), SiLU; q and k L2-normalised per head, q
+// scaled by 1/sqrt(dk), value head h reading q/k head h / (H / Hk); q, k, v
+// rounded to bf16; beta = sigmoid(b), g = -exp(A_log) softplus(a + dt_bias);
+// after the recurrence y = o / sqrt(mean(o^2) + eps) * norm_w * SiLU(z).
+struct MixArgs {
+    const __hip_bfloat16 *x;     // raw rows [B][T][conv_dim], channels q | k | v
+    const __hip_bfloat16 *hist;  // filter history [B][3][conv_dim], oldest first
+    const float *conv_w;         // [conv_dim][4]
+    const float *a, *bg;         // gate pre-activations [B][T][H]
+    const float *A_log, *dt_bias;  // [H]
+    const __hip_bfloat16 *z;     // output gate [B][T][H][dv]
+    const float *norm_w;         // [dv]
+    int Hk;                      // q/k heads
+};
+constexpr float kMixEps = 1e-6f;
+
+// Full-precision expf and sqrtf in the mixer (not the fast forms): q, k and v are
+// rounded to bf16 afterwards, and a smaller error moves fewer of them across a
+// rounding boundary.
+__device__ inline float silu(float x) { return x / (1.f + expf(-x)); }
+__device__ inline float softplusf(float x) { return x > 20.f ? x : log1pf(expf(x)); }
+__device__ inline uint32_t ldbits(const __hip_bfloat16 *p, size_t i) {
+    return reinterpret_cast<const uint16_t *>(p)[i];
+}
+// Sum over the wave, returned (uniform) to every lane: DPP within each row of 16
+// lanes (swap neighbours, swap pairs, mirror within 8, mirror within 16: every
+// lane then holds its row's sum), then the four row sums read out as scalars.
+// No LDS round trips, unlike a shuffle tree.
+template <int CTRL> __device__ inline float dpp_add(float v) {
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+__device__ inline float wave_sum(float v) {
+    v = dpp_add<0xB1>(v);    // quad_perm [1,0,3,2]
+    v = dpp_add<0x4E>(v);    // quad_perm [2,3,0,1]
+    v = dpp_add<0x141>(v);   // row_half_mirror
+    v = dpp_add<0x140>(v);   // row_mirror
+    const int u = __float_as_int(v);
+    return (__int_as_float(__builtin_amdgcn_readlane(u, 0)) + __int_as_float(__builtin_amdgcn_readlane(u, 16))) +
+           (__int_as_float(__builtin_amdgcn_readlane(u, 32)) + __int_as_float(__builtin_amdgcn_readlane(u, 48)));
+}
+
 // X rows: 0..TM-1 hold k_1..k_TM, TM..2TM-1 hold q_1..q_TM (TM = 8 MT); rows of
 // t >= T repeat row T (bf16: finite data nothing reads the results of) or are
 // zero (fp32).  MT = number of 16-row MFMA tiles of X (1 for T <= 8, 2 for
@@ -78,12 +122,15 @@ __device__ inline bf16x8 xrow_bf16(const uint8_t *Xb, int x, int p, int lg) {
 // few heads (a workgroup covers 32 rows, dv / 32 workgroups per head, each
 // computing the head's block coefficients itself): four times the workgroups,
 // a quarter of the state per wave.
-template <int DK, int DV, typename TIn, int MT, bool FUSED, int NT>
+//
+// MIX: q, k, v and the gates come from the mixer's raw inputs (`mix`) instead of
+// q, k, v, g, beta, and the outputs are the gated RMS norm of the recurrence's.
+template <int DK, int DV, typename TIn, int MT, bool FUSED, int NT, bool MIX = false>
 __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void verify_kernel(
     float *__restrict__ S, const TIn *__restrict__ q, const TIn *__restrict__ k,
     const TIn *__restrict__ v, const float *__restrict__ g, const float *__restrict__ beta,
     int T, int B, int H, float *__restrict__ o, uint8_t *__restrict__ rec, uint8_t *__restrict__ rprev,
-    const int32_t *__restrict__ n_acc, int32_t *__restrict__ pos) {
+    const int32_t *__restrict__ n_acc, int32_t *__restrict__ pos, MixArgs mix) {
     constexpr int NW = DV / 64;      // waves per workgroup
     constexpr int NTH = 64 * NW;     // threads
     constexpr int RW = 16 * NT;      // value rows per wave
@@ -103,12 +150,13 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void ve
     constexpr int NSTATE = NT * KM;  // state loads per thread
     static_assert(NW * 64 == DV && KH * NW == KM && SLICES * RS == DV && RS % kCommitRows == 0, "shape");
     static_assert(!kBf16 || (NBK >= 1 && NBV >= 1 && NSTATE <= 63), "copy blocks");
+    static_assert(!MIX || (kBf16 && DK == 128 && DV == 128 && NT == 4), "the mixer: bf16, d = 128, whole heads");
 
     __shared__ __attribute__((aligned(16))) float X[kBf16 ? 4 : XR * XS];
     __shared__ __attribute__((aligned(16))) uint8_t Xb[kBf16 ? XR * 2 * DK : 16];
     __shared__ __attribute__((aligned(16))) uint8_t Vb[kBf16 ? TM * DV * 2 : 16];   // bf16 [TM][DV]
     __shared__ __attribute__((aligned(16))) float Vs[kBf16 ? 4 : TM * DV];          // fp32 [TM][DV]
-    __shared__ float P[XR][RS + 1];               // [K;Q] S^T: rows x, columns value row (local)
+    __shared__ __attribute__((aligned(16))) float P[XR][RS + 1];   // [K;Q] S^T: rows x, columns value row (local)
     __shared__ float gpart[NW][XR][XR + 1];       // per-wave partial Gram matrices
     __shared__ float coefM[TM][TM + 1], coefN[TM][TM + 1];
     __shared__ float Gs[TM], gam[TM], bs[TM];
@@ -196,7 +244,18 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void ve
     // 1. Gates, copied into LDS (lane t of wave 0 copies g_t and beta_t): a
     //    register load would be sunk by the compiler to its use, behind a wait for
     //    the state.
-    if (w == 0) {
+    [[maybe_unused]] float alog = 0.f, dtb = 0.f;
+    if constexpr (MIX) {
+        // Raw a_t and b_t (activated once they land, after the state loads are
+        // issued).
+        if (w == 0) {
+            const size_t gi = size_t(b * T + min(lane, T - 1)) * H + h;
+            dma4(mix.a + gi, lds_addr(graw));
+            dma4(mix.bg + gi, lds_addr(braw));
+        }
+        alog = mix.A_log[h];
+        dtb = mix.dt_bias[h];
+    } else if (w == 0) {
         const size_t gi = size_t(b * T + min(lane, T - 1)) * H + h;
         dma4(g + gi, lds_addr(graw));
         dma4(beta + gi, lds_addr(braw));
@@ -205,7 +264,49 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void ve
     //    (1 KiB blocks, round robin over the waves); fp32: 8-element pieces into
     //    registers, staged below.
     In8<TIn> xin[kBf16 ? 1 : NCH], vin[kBf16 ? 1 : NVP];
-    if constexpr (kBf16) {
+    // MIX: the head's raw rows (its q, k and v channel segments, 256 bytes each,
+    // of the 3 history rows and of the TM block rows, the latter clamped to row
+    // T - 1) are copied into LDS, the history rows into Xb and the block rows
+    // into P: both are free until the filter has read them (Xb is written after
+    // the norm barrier, P in the tile loop).  Thread c later builds channel c of
+    // q, k and v for every token.  Its filter taps, and the output gate and norm
+    // weight of value row c, are register loads, issued here too; the gates are
+    // pinned (an empty asm that claims to change them) in the epilogue.
+    [[maybe_unused]] float4 mwt[MIX ? 3 : 1];
+    [[maybe_unused]] uint32_t zr[MIX ? TM : 1];
+    [[maybe_unused]] float nwr = 0.f;
+    constexpr int kRawRow = 3 * 256;    // bytes of a raw row's three segments (dk = dv = 128)
+    static_assert(!MIX || TM * kRawRow <= int(sizeof(P)), "block rows fit P");
+    static_assert(!MIX || 3 * kRawRow <= XR * 2 * DK, "history rows fit Xb");
+    if constexpr (MIX) {
+        const int grp = H / mix.Hk, hk = h / grp, c = tid;
+        const size_t cdim = size_t(2 * mix.Hk * DK + H * DV);
+        const size_t seg0 = size_t(hk) * DK, seg1 = size_t(mix.Hk + hk) * DK, seg2 = size_t(2 * mix.Hk) * DK + size_t(h) * DV;
+        // 16-byte piece p of the raw rows: row p / 48, segment (p % 48) / 16,
+        // elements 8 (p % 16) ..; 64 pieces per copy instruction.
+        constexpr int NPH = 3 * 48;                   // history pieces
+        constexpr int NJH = (NPH + 63) / 64, NJX = TM * 48 / 64;   // copy instructions
+        const uint32_t lh = lds_addr(Xb), lp = lds_addr(&P[0][0]);
+#pragma unroll
+        for (int jj = 0; jj < (NJH + NJX + NW - 1) / NW; ++jj) {
+            const int j = jj * NW + w;                 // history blocks first, then block rows
+            const bool hist = j < NJH;
+            const int p = 64 * (hist ? j : j - NJH) + lane, pr = p % 48, u = pr / 16;
+            const size_t off = (u == 0 ? seg0 : u == 1 ? seg1 : seg2) + 8 * (pr % 16);
+            if (hist) {
+                if (p < NPH) dma16(mix.hist + (size_t(b) * 3 + p / 48) * cdim + off, lh + j * 1024);
+            } else if (j < NJH + NJX) {
+                dma16(mix.x + (size_t(b) * T + min(p / 48, T - 1)) * cdim + off, lp + (j - NJH) * 1024);
+            }
+        }
+        mwt[0] = *reinterpret_cast<const float4 *>(mix.conv_w + (seg0 + c) * 4);
+        mwt[1] = *reinterpret_cast<const float4 *>(mix.conv_w + (seg1 + c) * 4);
+        mwt[2] = *reinterpret_cast<const float4 *>(mix.conv_w + (seg2 + c) * 4);
+        const int i = rbase + RW * w + lane;   // the thread's value row in the epilogue
+#pragma unroll
+        for (int t = 0; t < TM; ++t) zr[t] = ldbits(mix.z, (size_t(b * T + min(t, T - 1)) * H + h) * DV + i);
+        nwr = mix.norm_w[i];
+    } else if constexpr (kBf16) {
         const uint32_t lx = lds_addr(Xb), lv = lds_addr(Vb);
         // Block j of K (of Q) holds rows 1024 j / (2 dk) ..; wave w copies blocks
         // w, w + NW, ...  Lane l's piece sits at LDS row r, slot s and comes from
@@ -252,7 +353,7 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void ve
     //    tiles in flight and issues the next after writing one back, so that its
     //    reads and write-backs share the memory system instead of queueing as a
     //    read phase followed by a write phase.
-    constexpr int NPRE = FUSED ? (NT < 2 ? NT : 2) : NT;   // tiles loaded up front
+    constexpr int NPRE = (FUSED || MIX) ? (NT < 2 ? NT : 2) : NT;   // tiles loaded up front
     const float *Sw = S + (size_t(bh) * DV + rbase + RW * w + lr) * DK + 4 * lg;
     float4 sreg[NT][KM];
     auto load_tile = [&](int nt) {
@@ -268,6 +369,55 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void ve
     // order, so once at most that many are outstanding the copies have landed.
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(NPRE * KM));
     asm volatile("" ::: "memory");
+    if constexpr (MIX) {
+        __shared__ float nrm[2][NW][TM];
+        const int c = tid;
+        __syncthreads();   // every wave's raw-row copies have landed
+        asm volatile("" : "+v"(alog), "+v"(dtb));
+        if (w == 0) {   // the gates; wave 0 copied them and is their only reader until a barrier
+            graw[lane] = -expf(alog) * softplusf(graw[lane] + dtb);
+            braw[lane] = 1.f / (1.f + expf(-braw[lane]));
+        }
+        float y[3][TM];
+#pragma unroll
+        for (int u = 0; u < 3; ++u) {
+            float xr[TM + 3];
+#pragma unroll
+            for (int r = 0; r < TM + 3; ++r) {
+                const uint8_t *row = r < 3 ? Xb + r * kRawRow : reinterpret_cast<const uint8_t *>(&P[0][0]) + (r - 3) * kRawRow;
+                xr[r] = bf16_bits_to_f32(*reinterpret_cast<const uint16_t *>(row + u * 256 + 2 * c));
+            }
+#pragma unroll
+            for (int t = 0; t < TM; ++t)
+                y[u][t] = silu(mwt[u].x * xr[t] + mwt[u].y * xr[t + 1] + mwt[u].z * xr[t + 2] + mwt[u].w * xr[t + 3]);
+        }
+        // L2 norms of q and k per token over the head's dk channels (two waves).
+#pragma unroll
+        for (int t = 0; t < TM; ++t) {
+            const float sq = wave_sum(y[0][t] * y[0][t]), sk = wave_sum(y[1][t] * y[1][t]);
+            if (lane == 0) {
+                nrm[0][w][t] = sq;
+                nrm[1][w][t] = sk;
+            }
+        }
+        __syncthreads();
+        const float qs = 1.f / sqrtf(float(DK));
+#pragma unroll
+        for (int t = 0; t < TM; ++t) {
+            float sq = 0.f, sk = 0.f;
+#pragma unroll
+            for (int j = 0; j < NW; ++j) {
+                sq += nrm[0][j][t];
+                sk += nrm[1][j][t];
+            }
+            const __bf16 qv = static_cast<__bf16>(y[0][t] / sqrtf(sq + kMixEps) * qs);
+            const __bf16 kv = static_cast<__bf16>(y[1][t] / sqrtf(sk + kMixEps));
+            const int piece = c >> 3, e2 = (c & 7) * 2;
+            *reinterpret_cast<__bf16 *>(Xb + xoff<DK>(t, piece) + e2) = kv;
+            *reinterpret_cast<__bf16 *>(Xb + xoff<DK>(TM + t, piece) + e2) = qv;
+            reinterpret_cast<__bf16 *>(Vb)[t * DV + c] = static_cast<__bf16>(y[2][t]);
+        }
+    }
     if constexpr (!kBf16) {
         // Stage X and V (fp32); the piece index is clamped exactly as for the
         // loads: a thread past the end rewrites the last piece with the same data.
@@ -481,6 +631,8 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void ve
                 for (int m = 0; m < KM; ++m) *reinterpret_cast<float4 *>(Sw_out + 16 * m) = sreg[nt][m];
             }
             if (nt + NPRE < NT) load_tile(nt + NPRE);
+        } else if constexpr (MIX) {
+            if (nt + NPRE < NT) load_tile(nt + NPRE);
         }
         f32x4 acc[MT];
 #pragma unroll
@@ -525,6 +677,7 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void ve
 
     // Value rows (one per lane, lane < RW of each wave): forward substitution for
     // delta, then outputs.
+    float oo[MIX ? TM : 1];
     if (lane < RW) {
         const int li = RW * w + lane, i = rbase + li;
         float *Drec = reinterpret_cast<float *>(rec + RL.delta);
@@ -545,8 +698,34 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void ve
 #pragma unroll
                 for (int j = 0; j <= t; ++j) ot += coefN[t][j] * d[j];
                 const size_t idx = (size_t(b * T + t) * H + h) * DV + i;
-                o[idx] = ot;
+                if constexpr (MIX)
+                    oo[t] = ot;
+                else
+                    o[idx] = ot;
                 Drec[idx] = dt;
+            }
+        }
+    }
+
+    if constexpr (MIX) {
+        // Gated RMS norm over the head's dv outputs of each token: every lane holds
+        // one value row (the workgroup covers the head).
+        __shared__ float osq[NW][TM];
+#pragma unroll
+        for (int t = 0; t < TM; ++t) {
+            const float s2 = wave_sum(t < T ? oo[t] * oo[t] : 0.f);
+            if (lane == 0) osq[w][t] = s2;
+        }
+        __syncthreads();
+        const int i = rbase + RW * w + lane;
+#pragma unroll
+        for (int t = 0; t < TM; ++t) {
+            if (t < T) {
+                float s2 = 0.f;
+#pragma unroll
+                for (int j = 0; j < NW; ++j) s2 += osq[j][t];
+                const size_t idx = (size_t(b * T + t) * H + h) * DV + i;
+                o[idx] = oo[t] / sqrtf(s2 / float(DV) + kMixEps) * nwr * silu(__uint_as_float(zr[t] << 16));
             }
         }
     }
@@ -600,18 +779,18 @@ hipError_t launch_t(float *S, const void *q, const void *k, const void *v, const
         const dim3 grid(heads * unsigned(DV / 32));
         if (T <= 8)
             hipLaunchKernelGGL((verify_kernel<DK, DV, TIn, 1, FUSED, NTF>), grid, block, 0, st, S, qq, kk, vv, g,
-                               beta, T, s.B, s.H, o, rr, rp, n_acc, pos);
+                               beta, T, s.B, s.H, o, rr, rp, n_acc, pos, MixArgs{});
         else
             hipLaunchKernelGGL((verify_kernel<DK, DV, TIn, 2, FUSED, NTF>), grid, block, 0, st, S, qq, kk, vv, g,
-                               beta, T, s.B, s.H, o, rr, rp, n_acc, pos);
+                               beta, T, s.B, s.H, o, rr, rp, n_acc, pos, MixArgs{});
     } else {
         const dim3 grid(heads);
         if (T <= 8)
             hipLaunchKernelGGL((verify_kernel<DK, DV, TIn, 1, FUSED, 4>), grid, block, 0, st, S, qq, kk, vv, g,
-                               beta, T, s.B, s.H, o, rr, rp, n_acc, pos);
+                               beta, T, s.B, s.H, o, rr, rp, n_acc, pos, MixArgs{});
         else
             hipLaunchKernelGGL((verify_kernel<DK, DV, TIn, 2, FUSED, 4>), grid, block, 0, st, S, qq, kk, vv, g,
-                               beta, T, s.B, s.H, o, rr, rp, n_acc, pos);
+                               beta, T, s.B, s.H, o, rr, rp, n_acc, pos, MixArgs{});
     }
     return hipGetLastError();
 }
@@ -635,7 +814,52 @@ hipError_t launch_any(float *S, const void *q, const void *k, const void *v, con
     return hipErrorInvalidValue;
 }
 
+template <bool FUSED>
+hipError_t launch_mix_t(float *S, const MixArgs &m, int T, const gdn_shape &s, float *o, void *rec, void *rprev,
+                        const int32_t *n_acc, int32_t *pos, hipStream_t st) {
+    using bf = __hip_bfloat16;
+    const dim3 grid(unsigned(s.B) * unsigned(s.H)), block(128);
+    auto *rr = static_cast<uint8_t *>(rec);
+    auto *rp = static_cast<uint8_t *>(rprev);
+    const bf *none = nullptr;
+    const float *nonef = nullptr;
+    if (T <= 8)
+        hipLaunchKernelGGL((verify_kernel<128, 128, bf, 1, FUSED, 4, true>), grid, block, 0, st, S, none, none, none,
+                           nonef, nonef, T, s.B, s.H, o, rr, rp, n_acc, pos, m);
+    else
+        hipLaunchKernelGGL((verify_kernel<128, 128, bf, 2, FUSED, 4, true>), grid, block, 0, st, S, none, none, none,
+                           nonef, nonef, T, s.B, s.H, o, rr, rp, n_acc, pos, m);
+    return hipGetLastError();
+}
+
+MixArgs mix_args(const gdn_mixer_inputs &in) {
+    MixArgs m;
+    m.x = static_cast<const __hip_bfloat16 *>(in.x);
+    m.hist = static_cast<const __hip_bfloat16 *>(in.history);
+    m.conv_w = in.conv_w;
+    m.a = in.a;
+    m.bg = in.b;
+    m.A_log = in.A_log;
+    m.dt_bias = in.dt_bias;
+    m.z = static_cast<const __hip_bfloat16 *>(in.z);
+    m.norm_w = in.norm_w;
+    m.Hk = in.Hk;
+    return m;
+}
+
 }  // namespace
+
+hipError_t launch_mixer_verify(const float *S, const gdn_mixer_inputs &in, int T, const gdn_shape &shp, float *y,
+                               void *record, hipStream_t stream) {
+    return launch_mix_t<false>(const_cast<float *>(S), mix_args(in), T, shp, y, record, nullptr, nullptr, nullptr,
+                               stream);
+}
+
+hipError_t launch_mixer_commit_verify(float *S, void *record_prev, const int32_t *n_accepted, int32_t *pos,
+                                      const gdn_mixer_inputs &in, int T, const gdn_shape &shp, float *y,
+                                      void *record_next, hipStream_t stream) {
+    return launch_mix_t<true>(S, mix_args(in), T, shp, y, record_next, record_prev, n_accepted, pos, stream);
+}
 
 hipError_t launch_verify(const float *S, const void *q, const void *k, const void *v,
                          const float *g, const float *beta, int T, gdn_in_dtype dt,

@@ -38,6 +38,8 @@ EXPORTED = (
     "gdn_history_rewind",
     "gdn_attn_workspace_bytes",
     "gdn_attn_verify",
+    "gdn_mixer_verify",
+    "gdn_mixer_commit_verify",
     "gdn_strerror",
 )
 GDN_HISTORY_MAX = 16
@@ -56,6 +58,13 @@ class gdn_shape(ctypes.Structure):
 
 class gdn_accept_shape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("V", ctypes.c_int32)]
+
+
+class gdn_mixer_inputs(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("history", ctypes.c_void_p), ("conv_w", ctypes.c_void_p),
+                ("a", ctypes.c_void_p), ("b", ctypes.c_void_p), ("A_log", ctypes.c_void_p),
+                ("dt_bias", ctypes.c_void_p), ("z", ctypes.c_void_p), ("norm_w", ctypes.c_void_p),
+                ("Hk", ctypes.c_int32)]
 
 
 class gdn_attn_shape(ctypes.Structure):
@@ -92,6 +101,11 @@ def _load() -> ctypes.CDLL:
     lib.gdn_accept_sampled.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp, ctypes.c_float, ap, vp, vp, vp, sz, vp]
     lib.gdn_history_rewind.restype = ctypes.c_int
     lib.gdn_history_rewind.argtypes = [vp, vp, vp, i32, i32, i32, i32, ctypes.c_int, vp]
+    mp = ctypes.POINTER(gdn_mixer_inputs)
+    lib.gdn_mixer_verify.restype = ctypes.c_int
+    lib.gdn_mixer_verify.argtypes = [vp, mp, i32, sp, vp, vp, sz, vp]
+    lib.gdn_mixer_commit_verify.restype = ctypes.c_int
+    lib.gdn_mixer_commit_verify.argtypes = [vp, vp, vp, vp, mp, i32, sp, vp, vp, sz, vp]
     tp = ctypes.POINTER(gdn_attn_shape)
     lib.gdn_attn_workspace_bytes.restype = sz
     lib.gdn_attn_workspace_bytes.argtypes = [tp, i32]
@@ -371,3 +385,48 @@ def gdn_attn_verify(q, k_new, v_new, k_cache, v_cache, ctx, o, scale=None, ws=No
                              float(scale), ctypes.byref(shp), _ptr(o), _ptr(ws), nb, _stream(stream))
     if rc != 0:
         raise GdnError(rc, "gdn_attn_verify")
+
+
+def _mixer_struct(S, m, T):
+    """The C struct of a MixerInputs (speculative_verify_amd.inputs), after shape checks."""
+    B, H, dv, dk = S.shape
+    cdim = 2 * m.Hk * dk + H * dv
+    want = {"x": (m.x, (B, T, cdim), torch.bfloat16), "history": (m.history, (B, 3, cdim), torch.bfloat16),
+            "conv_w": (m.conv_w, (cdim, 4), torch.float32), "a": (m.a, (B, T, H), torch.float32),
+            "b": (m.b, (B, T, H), torch.float32), "A_log": (m.A_log, (H,), torch.float32),
+            "dt_bias": (m.dt_bias, (H,), torch.float32), "z": (m.z, (B, T, H, dv), torch.bfloat16),
+            "norm_w": (m.norm_w, (dv,), torch.float32)}
+    for name, (x, shape, dt) in want.items():
+        if tuple(x.shape) != shape or x.dtype != dt:
+            raise ValueError(f"{name} must be {dt} {shape}")
+    return gdn_mixer_inputs(*(ctypes.c_void_p(getattr(m, f).data_ptr()) for f in
+                              ("x", "history", "conv_w", "a", "b", "A_log", "dt_bias", "z", "norm_w")), m.Hk)
+
+
+def gdn_mixer_verify(S, m, y, record, stream=None) -> None:
+    """The verify with the GDN mixer around it (see gdn_mixer_verify in
+    include/gdn.h): y[:] = gated, normalised outputs; the record as for
+    gdn_verify_block."""
+    T = m.x.shape[1]
+    shp = _shape_of(S)
+    mi = _mixer_struct(S, m, T)
+    if tuple(y.shape) != (shp.B, T, shp.H, shp.dv) or y.dtype != torch.float32:
+        raise ValueError("y must be float32 [B][T][H][dv]")
+    rc = lib.gdn_mixer_verify(_ptr(S), ctypes.byref(mi), T, ctypes.byref(shp), _ptr(y), _ptr(record),
+                              record.numel() * record.element_size(), _stream(stream))
+    if rc != 0:
+        raise GdnError(rc, "gdn_mixer_verify")
+
+
+def gdn_mixer_commit_verify(S, record_prev, n_accepted, m, y, record_next, pos=None, stream=None) -> None:
+    """Commit of record_prev at n_accepted, then the mixer verify of the next block."""
+    T = m.x.shape[1]
+    shp = _shape_of(S)
+    mi = _mixer_struct(S, m, T)
+    if tuple(y.shape) != (shp.B, T, shp.H, shp.dv) or y.dtype != torch.float32:
+        raise ValueError("y must be float32 [B][T][H][dv]")
+    rc = lib.gdn_mixer_commit_verify(_ptr(S), _ptr(record_prev), _ptr(n_accepted), _ptr(pos), ctypes.byref(mi), T,
+                                     ctypes.byref(shp), _ptr(y), _ptr(record_next),
+                                     record_next.numel() * record_next.element_size(), _stream(stream))
+    if rc != 0:
+        raise GdnError(rc, "gdn_mixer_commit_verify")

@@ -188,3 +188,45 @@ def make_attn_inputs(B: int, T: int, Hq: int, Hkv: int, d: int, Lmax: int, ctx, 
     out = AttnInputs(randn(B, T, Hq, d), randn(B, T, Hkv, d), randn(B, T, Hkv, d), randn(B, Lmax, Hkv, d),
                      randn(B, Lmax, Hkv, d), torch.as_tensor(ctx, dtype=torch.int32).reshape(B).to(gen_dev))
     return out.to(device) if gen_dev != torch.device(device) else out
+
+
+# ---------------------------------------------------------------------------
+# GDN mixer inputs (the layer's raw in-projection rows and the mixer's
+# parameters; random, no trained weights): x and the filter history N(0,1) in
+# bf16; filter taps 0.5 N(0,1); the gate pre-activations a, b N(0,1); A_log and
+# dt_bias 0.5 N(0,1); the output gate z N(0,1) in bf16; the norm weight
+# 1 + 0.1 N(0,1).  conv_dim = 2 Hk d + H d.  Draw order as listed.
+# ---------------------------------------------------------------------------
+@dataclass
+class MixerInputs:
+    x: torch.Tensor        # bf16 [B][T][conv_dim]
+    history: torch.Tensor  # bf16 [B][3][conv_dim]
+    conv_w: torch.Tensor   # fp32 [conv_dim][4]
+    a: torch.Tensor        # fp32 [B][T][H]
+    b: torch.Tensor        # fp32 [B][T][H]
+    A_log: torch.Tensor    # fp32 [H]
+    dt_bias: torch.Tensor  # fp32 [H]
+    z: torch.Tensor        # bf16 [B][T][H][d]
+    norm_w: torch.Tensor   # fp32 [d]
+    Hk: int
+
+    def to(self, device) -> "MixerInputs":
+        f = ("x", "history", "conv_w", "a", "b", "A_log", "dt_bias", "z", "norm_w")
+        return MixerInputs(*(getattr(self, n).to(device) for n in f), self.Hk)
+
+    def block(self, r: int, T: int) -> "MixerInputs":
+        """Rows r T .. r T + T - 1 of a longer draw (the history left as drawn)."""
+        sl = lambda t: t[:, r * T:(r + 1) * T].contiguous()
+        return MixerInputs(sl(self.x), self.history, self.conv_w, sl(self.a), sl(self.b), self.A_log,
+                           self.dt_bias, sl(self.z), self.norm_w, self.Hk)
+
+
+def make_mixer_inputs(B: int, T: int, H: int, Hk: int, d: int = 128, *, seed: int = 0, device="cpu") -> MixerInputs:
+    gen = torch.Generator()
+    gen.manual_seed(int(seed) + 32452843)
+    cdim = 2 * Hk * d + H * d
+    rn = lambda *s: torch.randn(*s, generator=gen, dtype=torch.float32)
+    out = MixerInputs(rn(B, T, cdim).to(torch.bfloat16), rn(B, 3, cdim).to(torch.bfloat16), 0.5 * rn(cdim, 4),
+                      rn(B, T, H), rn(B, T, H), 0.5 * rn(H), 0.5 * rn(H), rn(B, T, H, d).to(torch.bfloat16),
+                      1.0 + 0.1 * rn(d), Hk)
+    return out.to(device)

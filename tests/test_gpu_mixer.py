@@ -1,0 +1,85 @@
+"""GPU parity of the verify with the GDN mixer fused around it
+(gdn_mixer_verify, gdn_mixer_commit_verify) against the fp64 oracles: the mixer
+prologue and epilogue of oracle/mixer_oracle.py around the recurrence of the C
+oracle.  Bars: outputs within 2e-3 and committed state within 1e-3 (worst-slab
+relative, as for the verify).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import mixer_oracle as M
+from speculative_verify_amd.inputs import make_inputs, make_mixer_inputs
+from tests._metrics import OUT_TOL, STATE_TOL, rel_err_outputs, rel_err_state
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+D = 128
+
+
+@pytest.fixture(scope="module")
+def G():
+    import speculative_verify_amd.gdn as G
+    assert torch.cuda.is_available(), "the gpu tests need a GPU"
+    return G
+
+
+def print_case(**kw):
+    print("case:", " ".join(f"{k}={v}" for k, v in kw.items()), flush=True)
+
+
+def ref_block(S0, mc, H):
+    """Oracle: prologue, verify outputs and the gated norm; the prologue's q, k,
+    v, g, beta returned for the commit."""
+    f = lambda t: t.float().numpy()
+    q, k, v, g, beta = M.prologue(f(mc.x), f(mc.history), f(mc.conv_w), f(mc.a), f(mc.b), f(mc.A_log),
+                                  f(mc.dt_bias), mc.Hk, D, H, D)
+    o = oracle.verify(S0, q, k, v, g, beta)
+    return M.epilogue(o, f(mc.z), f(mc.norm_w)), (q, k, v, g, beta)
+
+
+@pytest.mark.parametrize("B,H,Hk,T", [(2, 4, 2, 8), (1, 32, 16, 8), (2, 4, 4, 1), (1, 8, 2, 12)])
+def test_mixer_verify_then_commit(G, B, H, Hk, T):
+    print_case(test="mixer_verify", B=B, H=H, Hk=Hk, T=T, seed=B * 100 + H + T)
+    S0 = make_inputs(B, H, D, D, 1, seed=B * 100 + H + T, device=DEV).S0
+    m = make_mixer_inputs(B, T, H, Hk, D, seed=B * 100 + H + T, device=DEV)
+    y = torch.full((B, T, H, D), float("nan"), device=DEV)
+    S = S0.clone()
+    rec = G.new_record(S, T, torch.bfloat16)
+    G.gdn_mixer_verify(S, m, y, rec)
+    n = torch.tensor([(3 * b + 2) % (T + 1) for b in range(B)], dtype=torch.int32, device=DEV)
+    G.gdn_commit(S, rec, n)
+    torch.cuda.synchronize()
+    S0c = S0.cpu().double().numpy()
+    y_ref, qkv = ref_block(S0c, m.to("cpu"), H)
+    eo = rel_err_outputs(y, y_ref)
+    es = rel_err_state(S, oracle.commit(S0c, *qkv, n.cpu().numpy()))
+    print(f"  output err {eo:.2e} state err {es:.2e}", flush=True)
+    assert eo <= OUT_TOL and es <= STATE_TOL
+
+
+def test_mixer_commit_verify_two_blocks(G):
+    """Block 0 by gdn_mixer_verify, then block 1 by gdn_mixer_commit_verify at
+    n = 5: the outputs of block 1 come from S_5 of block 0, and a final commit
+    of block 1 at n = 3 lands on the oracle's state."""
+    B, H, Hk, T = 2, 8, 4, 8
+    print_case(test="mixer_commit_verify", B=B, H=H, Hk=Hk, T=T, seed=21)
+    S0 = make_inputs(B, H, D, D, 1, seed=21, device=DEV).S0
+    full = make_mixer_inputs(B, 2 * T, H, Hk, D, seed=21, device=DEV)
+    m0, m1 = full.block(0, T), full.block(1, T)
+    S = S0.clone()
+    ra, rb = G.new_record(S, T, torch.bfloat16), G.new_record(S, T, torch.bfloat16)
+    y0 = torch.empty(B, T, H, D, device=DEV)
+    y1 = torch.empty(B, T, H, D, device=DEV)
+    G.gdn_mixer_verify(S, m0, y0, ra)
+    G.gdn_mixer_commit_verify(S, ra, torch.full((B,), 5, dtype=torch.int32, device=DEV), m1, y1, rb)
+    G.gdn_commit(S, rb, torch.full((B,), 3, dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    S0c = S0.cpu().double().numpy()
+    _, qkv0 = ref_block(S0c, m0.to("cpu"), H)
+    S5 = oracle.commit(S0c, *qkv0, np.full(B, 5, np.int32))
+    y1_ref, qkv1 = ref_block(S5, m1.to("cpu"), H)
+    S_ref = oracle.commit(S5, *qkv1, np.full(B, 3, np.int32))
+    assert rel_err_outputs(y1, y1_ref) <= OUT_TOL
+    assert rel_err_state(S, S_ref) <= STATE_TOL
