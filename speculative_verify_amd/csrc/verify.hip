@@ -83,10 +83,28 @@ struct MixArgs {
 };
 constexpr float kMixEps = 1e-6f;
 
-// Full-precision expf and sqrtf in the mixer (not the fast forms): q, k and v are
-// rounded to bf16 afterwards, and a smaller error moves fewer of them across a
-// rounding boundary.
-__device__ inline float silu(float x) { return x / (1.f + expf(-x)); }
+// SiLU per element of the mixer, in about a dozen instructions and within about
+// 1 ulp: e^-x from the hardware exp2 with the rounding error of -x log2(e)
+// (carried in two parts) folded back in to first order, and the reciprocal of
+// 1 + e^-x from the hardware estimate refined by one Newton step.  q, k and v
+// are rounded to bf16 afterwards: a smaller error moves fewer of them across a
+// rounding boundary.  x is clamped at -40 (where x sigmoid(x) is below 2e-16 in
+// size) so that no step meets an infinity.
+__device__ inline float silu(float x) {
+    constexpr float kL2e = 1.44269504f, kL2eLo = 1.925963e-8f, kLn2 = 0.693147181f;
+    const float xc = fmaxf(x, -40.f);
+    const float t = -xc * kL2e;
+    const float lo = fmaf(-xc, kL2eLo, fmaf(-xc, kL2e, -t));   // -xc log2(e) - t
+    const float d = 1.f + __builtin_amdgcn_exp2f(t) * fmaf(lo, kLn2, 1.f);
+    float r = __builtin_amdgcn_rcpf(d);
+    r *= fmaf(-d, r, 2.f);
+    return x * r;
+}
+// 1 / sqrt(a) for a > 0: the hardware estimate and one Newton step.
+__device__ inline float rsqrt_nr(float a) {
+    const float r = __builtin_amdgcn_rsqf(a);
+    return r * fmaf(-0.5f * a * r, r, 1.5f);
+}
 __device__ inline float softplusf(float x) { return x > 20.f ? x : log1pf(expf(x)); }
 __device__ inline uint32_t ldbits(const __hip_bfloat16 *p, size_t i) {
     return reinterpret_cast<const uint16_t *>(p)[i];
@@ -376,7 +394,7 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void ve
         asm volatile("" : "+v"(alog), "+v"(dtb));
         if (w == 0) {   // the gates; wave 0 copied them and is their only reader until a barrier
             graw[lane] = -expf(alog) * softplusf(graw[lane] + dtb);
-            braw[lane] = 1.f / (1.f + expf(-braw[lane]));
+            braw[lane] = 1.f / (1.f + expf(-braw[lane]));   // once per token: the library forms
         }
         float y[3][TM];
 #pragma unroll
@@ -401,7 +419,7 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void ve
             }
         }
         __syncthreads();
-        const float qs = 1.f / sqrtf(float(DK));
+        const float qs = 1.f / sqrtf(float(DK));   // a constant
 #pragma unroll
         for (int t = 0; t < TM; ++t) {
             float sq = 0.f, sk = 0.f;
@@ -410,8 +428,8 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void ve
                 sq += nrm[0][j][t];
                 sk += nrm[1][j][t];
             }
-            const __bf16 qv = static_cast<__bf16>(y[0][t] / sqrtf(sq + kMixEps) * qs);
-            const __bf16 kv = static_cast<__bf16>(y[1][t] / sqrtf(sk + kMixEps));
+            const __bf16 qv = static_cast<__bf16>(y[0][t] * (rsqrt_nr(sq + kMixEps) * qs));
+            const __bf16 kv = static_cast<__bf16>(y[1][t] * rsqrt_nr(sk + kMixEps));
             const int piece = c >> 3, e2 = (c & 7) * 2;
             *reinterpret_cast<__bf16 *>(Xb + xoff<DK>(t, piece) + e2) = kv;
             *reinterpret_cast<__bf16 *>(Xb + xoff<DK>(TM + t, piece) + e2) = qv;
@@ -725,7 +743,7 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void ve
 #pragma unroll
                 for (int j = 0; j < NW; ++j) s2 += osq[j][t];
                 const size_t idx = (size_t(b * T + t) * H + h) * DV + i;
-                o[idx] = oo[t] / sqrtf(s2 / float(DV) + kMixEps) * nwr * silu(__uint_as_float(zr[t] << 16));
+                o[idx] = oo[t] * rsqrt_nr(s2 * (1.f / float(DV)) + kMixEps) * nwr * silu(__uint_as_float(zr[t] << 16));
             }
         }
     }
