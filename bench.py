@@ -93,6 +93,18 @@ def fused_bytes(B, H, dk, dv, T, n, es):
     return verify_bytes(B, H, dk, dv, T, es) + extra
 
 
+def mixer_fused_bytes(B, H, Hk, d, T, n):
+    """Algorithmic HBM bytes of one gdn_mixer_commit_verify launch at accepted
+    length n: those of gdn_commit_verify with bf16 inputs, with the block's q, k,
+    v replaced by the raw rows (q/k channels once per q/k head), the filter
+    history, the output gate z, and the filter taps and norm weight; the gate
+    pre-activations a, b take the place of g, beta byte for byte."""
+    cdim = 2 * Hk * d + H * d
+    qkv = B * T * H * 3 * d * 2
+    raw = B * T * cdim * 2 + B * 3 * cdim * 2 + B * T * H * d * 2 + cdim * 16 + d * 4 + H * 8
+    return fused_bytes(B, H, d, d, T, n, 2) - qkv + raw
+
+
 def prefill_bytes(B, H, dk, dv, L):
     return B * L * H * (2 * dk + dv) * 2 + B * L * H * 8 + B * L * H * dv * 4 + 2 * B * H * dv * dk * 4
 
@@ -728,40 +740,53 @@ def bench_mixer(args, G, dev):
     """The 48-layer pass with the GDN mixer fused around the recurrence: one
     gdn_mixer_commit_verify per pass (filter, norms and gates from the raw
     in-projection rows; gated RMS norm on the outputs) against one
-    gdn_commit_verify on ready q, k, v, at the same accepted lengths."""
+    gdn_commit_verify on ready q, k, v, at the same accepted lengths.  Four state
+    buffers rotate, as in the headline, so that no launch finds its state still in
+    the last-level cache."""
     import torch
 
     from speculative_verify_amd.inputs import make_accepts, make_inputs, make_mixer_inputs
 
-    L, H = LAYERS, HEADS
+    L, H, NSET = LAYERS, HEADS, 4
     x = make_inputs(L, H, DK, DV, T, seed=args.seed + 61, device=dev, device_gen=True)
     m = make_mixer_inputs(L, T, H, MIX_HK, DK, seed=args.seed + 61, device=dev)
     ns = make_accepts(64, T, seed=args.seed + 61)
     nt = [torch.full((L,), int(v), dtype=torch.int32, device=dev) for v in ns]
     y = torch.empty(L, T, H, DV, dtype=torch.float32, device=dev)
-    S = x.S0.clone()
-    recs = [G.new_record(S, T, torch.bfloat16) for _ in range(2)]
+    Ss = [x.S0.clone() for _ in range(NSET)]
+    recs = [[G.new_record(Ss[j], T, torch.bfloat16) for _ in range(2)] for j in range(NSET)]
     out = {"workload": f"{L} GDN layers x {H} value heads ({MIX_HK} q/k heads), d={DK}, T={T}: commit + verify "
-                       f"per pass, n~U{{0..8}}"}
+                       f"per pass, n~U{{0..8}}, {NSET} rotating state buffers"}
     for name in ("mixer_commit_verify", "commit_verify"):
-        if name == "mixer_commit_verify":
-            G.gdn_mixer_verify(S, m, y, recs[0])
-            step = lambda i: G.gdn_mixer_commit_verify(S, recs[i % 2], nt[i % len(nt)], m, y, recs[(i + 1) % 2])
-        else:
-            G.gdn_verify_block(S, x.q, x.k, x.v, x.g, x.beta, y, recs[0])
-            step = lambda i: G.gdn_commit_verify(S, recs[i % 2], nt[i % len(nt)], x.q, x.k, x.v, x.g, x.beta, y,
-                                                 recs[(i + 1) % 2])
-        for i in range(10):
+        def step(i):
+            j, c = i % NSET, i // NSET
+            rp, rn = recs[j][c % 2], recs[j][(c + 1) % 2]
+            if name == "mixer_commit_verify":
+                G.gdn_mixer_commit_verify(Ss[j], rp, nt[i % len(nt)], m, y, rn)
+            else:
+                G.gdn_commit_verify(Ss[j], rp, nt[i % len(nt)], x.q, x.k, x.v, x.g, x.beta, y, rn)
+        for j in range(NSET):   # a pending block on every set
+            if name == "mixer_commit_verify":
+                G.gdn_mixer_verify(Ss[j], m, y, recs[j][0])
+            else:
+                G.gdn_verify_block(Ss[j], x.q, x.k, x.v, x.g, x.beta, y, recs[j][0])
+        for i in range(12):
             step(i)
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         n = 100
         a.record()
-        for i in range(10, 10 + n):
+        for i in range(12, 12 + n):
             step(i)
         b.record()
         torch.cuda.synchronize()
-        out[name + "_us"] = round(a.elapsed_time(b) / n * 1e3, 2)
+        us = a.elapsed_time(b) / n * 1e3
+        out[name + "_us"] = round(us, 2)
+        nv = [int(ns[i % len(ns)]) for i in range(12, 12 + n)]
+        nb = [mixer_fused_bytes(L, H, MIX_HK, DK, T, v) if name == "mixer_commit_verify" else
+              fused_bytes(L, H, DK, DV, T, v, 2) for v in nv]
+        out[name + "_bytes"] = int(sum(nb) / n)
+        out[name + "_tbs"] = round(sum(nb) / n / us * 1e-6, 3)
     return out
 
 

@@ -318,10 +318,10 @@ int gdn_history_rewind(void *history, const void *rows, const int32_t *n, int32_
 /* ---------------------------------------------------------------------------
  * The GDN mixer around the recurrence, fused into the verify.
  *
- * Source: the README page ("How it works", region table, "GDN mixer" row): the
- * mixer's megakernel coordinates projections, recurrence, gating and
- * normalisation through their dependencies; the audited-numbers page (DSpark
- * section): a small filter layer keeps a short history of its inputs.  The pages
+ * Source: the README page ("How it works", region table, "GDN mixer" row): one
+ * megakernel runs the layer's projections, recurrence, gating and normalisation
+ * in dependency order; the audited-numbers page (DSpark section): a filter
+ * before the mixer holds its last few inputs, which a rewind restores.  The pages
  * give no formulas; these follow the published Gated DeltaNet layer (ICLR 2025)
  * as deployed in the Qwen3-Next hybrid.  Per token, from the layer's raw
  * in-projection row x (conv_dim = 2 Hk dk + H dv channels: q heads | k heads |

@@ -10,8 +10,8 @@ token is kept only where it equals the target model's token; in sampled mode it
 is kept with probability min(1, p/q) (target probability over drafter
 probability); the pass then emits a correction token at the first rejection, or
 a bonus token when every draft was kept.  Rewind follows: the key-value cache,
-the short history of the small filter layer and the recurrent state are brought
-back in line with the kept tokens.  The README page ("How it works") keeps
+the last few inputs held by the filter before the mixer, and the recurrent state
+all return to the kept tokens.  The README page ("How it works") keeps
 positions, accepted tokens and commit/rollback on the GPU.
 
 Readings (where the pages leave a step open):

@@ -4,10 +4,10 @@ infrastructure only.
 Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
 import this module.  It shares no code with the HIP library.
 
-Source: the README page ("How it works", region table, "GDN mixer" row): the
-mixer's megakernel coordinates the projections, the recurrence, the gating and
-the normalisation; the audited-numbers page (DSpark section): a small filter
-layer keeps a short history of its inputs.  The pages give no formulas.  The
+Source: the README page ("How it works", region table, "GDN mixer" row): one
+megakernel runs the layer's projections, recurrence, gating and normalisation
+in dependency order; the audited-numbers page (DSpark section): a filter before
+the mixer holds its last few inputs, which a rewind restores.  The pages give no formulas.  The
 readings below follow the published Gated DeltaNet layer (Yang, Kautz &
 Hatamizadeh, ICLR 2025), as deployed in the Qwen3-Next hybrid:
 
