@@ -197,3 +197,34 @@ def test_attn_rejects_bad_arguments(G):
     assert call(wsb=16) == -4
     assert L.gdn_attn_workspace_bytes(shp(), 8) > 0
     assert L.gdn_attn_workspace_bytes(shp(d=64), 8) == 0
+
+
+def test_mixer_rejects_bad_arguments(G):
+    L = G.lib
+
+    def mix(Hk=2, **kw):
+        f = {n: FAKE for n in ("x", "history", "conv_w", "a", "b", "A_log", "dt_bias", "z", "norm_w")}
+        f.update(kw)
+        return ctypes.byref(G.gdn_mixer_inputs(*(f[n] for n in ("x", "history", "conv_w", "a", "b", "A_log",
+                                                                 "dt_bias", "z", "norm_w")), Hk))
+
+    def call(m=None, T=8, shp=None, S=FAKE, rec_bytes=1 << 30):
+        return L.gdn_mixer_verify(S, m or mix(), T, shp or _shape(1, 4, 128, 128), FAKE, FAKE, rec_bytes, None)
+
+    def fused(rp=FAKE, rn=ctypes.c_void_p(1 << 31), nb=1 << 20):
+        return L.gdn_mixer_commit_verify(FAKE, rp, FAKE, None, mix(), 8, _shape(1, 4, 128, 128), FAKE, rn, nb, None)
+
+    assert L.gdn_mixer_verify(FAKE, None, 8, _shape(1, 4, 128, 128), FAKE, FAKE, 1 << 30, None) == -1
+    assert call(S=None) == -1
+    assert call(m=mix(x=None)) == -1
+    assert call(m=mix(x=FAKE_ODD)) == -1          # raw rows are copied in 16-byte pieces
+    assert call(m=mix(history=FAKE_ODD)) == -1
+    assert call(m=mix(norm_w=None)) == -1
+    assert call(shp=_shape(1, 4, 64, 64)) == -2    # d = 128 only
+    assert call(m=mix(Hk=3)) == -2                  # H not a multiple of Hk
+    assert call(m=mix(Hk=0)) == -2
+    assert call(T=0) == -3
+    assert call(T=17) == -3
+    assert call(rec_bytes=16) == -4
+    assert fused(rn=FAKE) == -1                     # the two records overlap
+    assert fused(nb=16) == -4
