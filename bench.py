@@ -36,6 +36,7 @@ KERNEL_SOURCES = ["speculative_verify_amd/csrc/verify.hip", "speculative_verify_
 # Workload sizes.
 LAYERS, HEADS, DK, DV, T = 48, 32, 128, 128, 8
 PF_B, PF_H, PF_L, PF_C = 1, 32, 4096, 64
+PFL_B, PFL_L = 48, 32768   # the long-context prompt: all 48 GDN layers, 32K tokens
 RING, LAG = 4, 2
 
 
@@ -51,6 +52,8 @@ def parse():
     p.add_argument("--no-accept", action="store_true")
     p.add_argument("--no-attn", action="store_true")
     p.add_argument("--no-mixer", action="store_true")
+    p.add_argument("--no-prefill-long", action="store_true",
+                   help="skip the 48-layer, 32,768-token prefill (about 65 GB of device memory)")
     p.add_argument("--decode-steps", type=int, default=10000)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget-s", type=float, default=15.0)
@@ -128,6 +131,22 @@ def sources_hash():
 
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "hbm_traffic_verify_commit_48x32_T8_prefill_32x4096.json")
 STATS_MD = os.path.join(ROOT, "profiles", "kernel_stats_verify_commit_48x32_T8_prefill_32x4096.md")
+MFMA_JSON = os.path.join(ROOT, "profiles", "mfma_prefill_32x4096_and_48x32x32768.json")
+
+
+def load_mfma(leg):
+    """The MFMA counter summary of a prefill leg, only if it was taken on the
+    current kernel sources."""
+    try:
+        with open(MFMA_JSON) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("sources_sha256_16") != sources_hash():
+        return None
+    k = t.get("legs", {}).get(leg)
+    return None if k is None else {c: k[c] for c in ("executed_over_algorithmic", "executed_frac_of_peak",
+                                                     "mfma_busy_frac")}
 
 
 def load_traffic(kernel):
@@ -411,6 +430,8 @@ def main():
     result["copy_ceiling"] = copy_ceiling(dev)
     if not args.no_prefill:
         result["prefill"] = bench_prefill(args, G, dev)
+    if not args.no_prefill_long:
+        result["prefill_long"] = bench_prefill(args, G, dev, B=PFL_B, L=PFL_L, reps=3, flush_mib=0, traffic_key=None)
     if not args.no_decode:
         result["decode"] = bench_decode(args, G, dev)
     if not args.no_accept:
@@ -482,8 +503,9 @@ def summarize_profiles(args):
 
     # Kernel-trace statistics.
     stats = _read_csv(os.path.join(d, "stats", "**", "*kernel_stats.csv"))
-    lines = ["# Kernel time: verify + commit (48 layers x 32 heads, d=128, T=8), chunked "
-             "prefill (32 heads, L=4096), plain decode (32 heads, T=1) and acceptance (T=8, V=151,936)", "",
+    lines = ["# Kernel time: verify + commit (48 layers x 32 heads, d=128, T=8), the same pass with the GDN "
+             "mixer, chunked prefill (32 heads, L=4096; 48 layers x 32 heads, L=32768), plain decode (32 heads, "
+             "T=1), acceptance (T=8, V=151,936) and full attention (16 layers, 32,760 cached positions)", "",
              "rocprofv3 `--kernel-trace --stats` of the benchmark, GPU kernels of libgdn only "
              "(torch's input generation and copies omitted).", "", "Command:", "", "```",
              commands[0], "```", "", "| kernel | calls | average us | min us | max us | share of listed time |",
@@ -555,12 +577,12 @@ def summarize_profiles(args):
     # regions); the separate commits run passes warmup + 2 steps + i.
     # (Four tiles a wave: the 48-layer launches; the plain-decode leg's few-heads
     # launches are not in the counter runs.)
-    fus = kernel_rows("verify_kernel", ", true, 4>")
+    fus = kernel_rows("verify_kernel", ", true, 4, false>")
     if fus:
         fus = fus[:total]
         summary["kernels"]["commit_verify_kernel"] = summarize(
             fus, [fused_bytes(LAYERS, HEADS, DK, DV, T, n_host[i], es) for i in range(len(fus))])
-    ver = kernel_rows("verify_kernel", ", false, 4>")
+    ver = kernel_rows("verify_kernel", ", false, 4, false>")
     if ver:
         vb = verify_bytes(LAYERS, HEADS, DK, DV, T, es)
         fr = sum(r[1] for r in ver) / len(ver)
@@ -594,6 +616,58 @@ def summarize_profiles(args):
         json.dump(summary, f, indent=1)
         f.write("\n")
     print(f"wrote {STATS_MD} and {TRAFFIC_JSON}")
+    if os.path.isdir(os.path.join(d, "mfma")):
+        summarize_mfma(d, commands, src_hash)
+
+
+def summarize_mfma(d, commands, src_hash):
+    """MFMA counters of the prefill calls (the bf16 MFMA operations executed, and
+    the matrix pipes' busy cycles against the kernel's active cycles), from a
+    --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE run
+    The calls' durations come from the plain benchmark run of the same tree
+    (bench.json: counter collection slows the calls down), else from the counter
+    run's own output (mfma.json).  GRBM_GUI_ACTIVE reads the sum over the 8 XCDs
+    of the active cycles; the busy cycles are summed over the 1,024 SIMDs."""
+    rows = _read_csv(os.path.join(d, "mfma", "**", "*counter_collection.csv"))
+    disp = {}
+    for r in rows:
+        e = disp.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"]})
+        e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    bench_out, timed_by = None, None
+    for name in ("bench.json", "mfma.json"):
+        try:
+            with open(os.path.join(d, name)) as f:
+                bench_out, timed_by = json.loads(f.read().strip().splitlines()[-1]), name
+            break
+        except (OSError, ValueError, IndexError):
+            continue
+    if bench_out is None:
+        raise SystemExit("no benchmark output next to the MFMA counters")
+    out = {"sources_sha256_16": src_hash, "command": next((c for c in commands if "--pmc SQ_INSTS_VALU_MFMA" in c), None),
+           "durations_from": "plain benchmark run" if timed_by == "bench.json" else "the counter run", "legs": {}}
+    for leg, tags in (("prefill", ("prefill_prep_kernel", "prefill_stage_kernel")),
+                      ("prefill_long", ("prefill_kernel<",))):
+        ds = [e for e in disp.values() if any(t in e["name"] for t in tags)]
+        b = bench_out.get(leg, {})
+        if not ds or "avg_launch_us" not in b:
+            continue
+        calls = sum(1 for e in ds if tags[0] in e["name"])
+        flops = sum(e.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) for e in ds) * 512 / calls
+        busy = sum(e.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) for e in ds)
+        active = sum(e.get("GRBM_GUI_ACTIVE", 0.0) for e in ds) / 8 * 1024
+        us = b["avg_launch_us"]
+        out["legs"][leg] = {
+            "workload": b.get("workload"), "calls": calls, "avg_launch_us": us,
+            "mfma_bf16_flops_executed_per_call": round(flops),
+            "algorithmic_flops_per_call": round(b["mfma"]["flops_per_launch"]),
+            "executed_over_algorithmic": round(flops / b["mfma"]["flops_per_launch"], 3),
+            "executed_tflops": round(flops / (us * 1e-6) / 1e12, 2),
+            "executed_frac_of_peak": round(flops / (us * 1e-6) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+            "mfma_busy_frac": round(busy / active, 4) if active else None}
+    with open(MFMA_JSON, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(f"wrote {MFMA_JSON}")
 
 
 def bench_decode(args, G, dev):
@@ -832,25 +906,30 @@ def bench_attn(args, G, dev):
     return out
 
 
-def bench_prefill(args, G, dev):
+def bench_prefill(args, G, dev, B=PF_B, L=PF_L, reps=None, flush_mib=512, traffic_key="prefill"):
+    """Chunked prefill of B layers x PF_H heads over an L-token prompt, timed with
+    events over `reps` calls; a token counts once it has passed all B layers."""
     import torch
 
     from speculative_verify_amd.inputs import make_inputs
 
-    x = make_inputs(PF_B, PF_H, DK, DV, PF_L, seed=args.seed + 77, device=dev, device_gen=True)
-    o = torch.empty(PF_B, PF_L, PF_H, DV, dtype=torch.float32, device=dev)
+    reps = args.prefill_reps if reps is None else reps
+    x = make_inputs(B, PF_H, DK, DV, L, seed=args.seed + 77, device=dev, device_gen=True)
+    o = torch.empty(B, L, PF_H, DV, dtype=torch.float32, device=dev)
     S = x.S0.clone()
-    need = G.gdn_prefill_workspace_bytes(S, PF_L, PF_C)
+    need = G.gdn_prefill_workspace_bytes(S, L, PF_C)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev) if need else None
     try:
         G.gdn_prefill_chunked(S, x.q, x.k, x.v, x.g, x.beta, o, chunk=PF_C, ws=ws)
     except G.GdnError as e:
         return {"status": f"unavailable: {e}"}
-    # A 512 MiB buffer rewritten between reps pushes the prompt out of the caches.
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    # A buffer rewritten between reps pushes the prompt out of the caches (not
+    # needed when the prompt itself is many times the cache).
+    flush = torch.empty(flush_mib << 20, dtype=torch.uint8, device=dev) if flush_mib else None
     t_ms = []
-    for _ in range(args.prefill_reps):
-        flush.fill_(1)
+    for _ in range(reps):
+        if flush is not None:
+            flush.fill_(1)
         S.copy_(x.S0)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
@@ -858,22 +937,25 @@ def bench_prefill(args, G, dev):
         b.record()
         torch.cuda.synchronize()
         t_ms.append(a.elapsed_time(b))
+    del x, o, S, ws, flush
+    torch.cuda.empty_cache()
     avg = sum(t_ms) / len(t_ms)
-    fl = prefill_flops(PF_B, PF_H, DK, DV, PF_L, PF_C)
-    by = prefill_bytes(PF_B, PF_H, DK, DV, PF_L)
+    fl = prefill_flops(B, PF_H, DK, DV, L, PF_C)
+    by = prefill_bytes(B, PF_H, DK, DV, L)
     tf = fl / (avg * 1e-3) / 1e12
     gbs = by / (avg * 1e-3) / 1e9
-    return {"workload": f"chunked prefill: {PF_B} layer x {PF_H} heads, dk=dv={DK}, L={PF_L}, chunk {PF_C}, "
-                        f"bf16 in, fp32 state, cold caches",
+    return {"workload": f"chunked prefill: {B} layer{'s' if B > 1 else ''} x {PF_H} heads, dk=dv={DK}, L={L}, "
+                        f"chunk {PF_C}, bf16 in, fp32 state, cold caches",
             "schedule": "two-phase (chunk prep, scan; prep of each segment beside the scan of the previous)" if need else "one-pass",
-            "workspace_bytes": need,
-            "tokens_per_s": round(PF_L / (avg * 1e-3), 1), "avg_launch_us": round(avg * 1e3, 2),
+            "workspace_bytes": need, "reps": reps,
+            "tokens_per_s": round(L / (avg * 1e-3), 1), "avg_launch_us": round(avg * 1e3, 2),
             "mfma": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
                      "flops_per_launch": fl, "flop_convention": "causal"},
             "hbm": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_launch": by,
-                    "traffic": load_traffic("prefill")}}
+                    "traffic": load_traffic(traffic_key) if traffic_key else None},
+            "mfma_counters": load_mfma("prefill" if B == PF_B and L == PF_L else "prefill_long")}
 
 
 if __name__ == "__main__":
