@@ -80,15 +80,14 @@ struct alignas(16) Smem {
     float Am[C][C + 4];     // strictly-lower(beta_t Gamma_tj k_t.k_j)
     float Tm[C][C + 4];     // Linv = (I + A)^{-1}
     float Pm[C][C + 4];     // lower-incl(Gamma_tj q_t.k_j)
-    float Wb[3][16][20];    // block-inverse scratch
     float gam[C], ee[C], bet[C], G[C];
     // Linv and P split into bf16 high and low parts: the A operands of the
     // state-coupled products, ready to use.
     __bf16 LiH[C][C + 8], LiL[C][C + 8], PH[C][C + 8], PL[C][C + 8];
 };
 
-// LDS of the prep kernel: Linv and its scratch reuse the keys' and queries'
-// space once the Gram matrices are built, so two workgroups fit on a CU.
+// LDS of the prep kernel: Linv and the inverse's scratch reuse the keys' and
+// queries' space once the Gram matrices are built, so two workgroups fit on a CU.
 template <int DK>
 struct alignas(16) PrepSmem {
     union {
@@ -98,7 +97,7 @@ struct alignas(16) PrepSmem {
         };
         struct {
             float Tm[C][C + 4];
-            float Wb[3][16][20];
+            float Inv[4 * 2 * 320];   // the inverse's scratch (4 waves x 2 matrices)
         };
     };
     float Am[C][C + 4];
@@ -173,12 +172,99 @@ __device__ inline void chunk_gates(SM &sm, float gt, float bt, int n, int lane) 
     sm.bet[lane] = bt;
 }
 
-// Gram matrices and Linv of the staged chunk (all NWS waves; barriers inside).
-// On entry Ks, Qs and the gates are in LDS; on exit Pm and Tm hold P and Linv in
-// their lower block triangles (diagonal blocks included, zero above the
-// diagonal within them); the strictly upper blocks are never written.
-template <int DK, int NWS, typename SM>
-__device__ inline void chunk_prep(SM &sm, int tid, int w, int lane) {
+// One 16x16 fp32 product on the fp32 MFMA, d + A B, with A(r, c) and B(r, c)
+// read through accessors: k-step s takes contraction index 4s + lg from lane
+// group lg.  The result is in the D layout: lane (lr, lg) holds rows 4lg .. 4lg + 3
+// of column lr.
+template <typename FA, typename FB>
+__device__ inline f32x4 mm16(FA a, FB b, f32x4 d, int lr, int lg) {
+    float av[4], bv[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        av[s] = a(lr, 4 * s + lg);
+        bv[s] = b(4 * s + lg, lr);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) d = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s], bv[s], d, 0, 0, 0);
+    return d;
+}
+
+// A D-layout tile into a wave's scratch matrix, stored transposed (column c at
+// 20 c): one 16-byte write per lane; read back through scr_at.
+__device__ inline void scr_put(float *m, const f32x4 &d, int lr, int lg) {
+    *reinterpret_cast<float4 *>(m + 20 * lr + 4 * lg) = make_float4(d[0], d[1], d[2], d[3]);
+}
+__device__ inline auto scr_at(const float *m) {
+    return [m](int r, int c) { return m[20 * c + r]; };
+}
+
+// Linv = (I + A)^{-1} for the chunk's strictly lower A (fp32 [C][C + 4] in LDS)
+// into Tm's lower block triangle, on the fp32 MFMA; waves 0..3 take part, and
+// any further waves run `side` meanwhile.
+// Diagonal 16x16 blocks: with N strictly lower, N^16 = 0 and
+//   (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8),
+// three squarings and three products, one wave per block, its intermediates in
+// its own two scratch matrices (scr: 4 x 2 x 320 floats).  Off-diagonal blocks,
+// one block diagonal d at a time (block row i = j + d):
+//   X_ij = -X_ii sum_{m=j}^{i-1} A_im X_mj.
+// Every product of lower-triangular factors keeps exact zeros above the
+// diagonal and ones on it, so the diagonal blocks need no masking.
+template <typename MA, typename MT, typename Side>
+__device__ inline void tri_inverse(const MA &Am, MT &Tm, float *scr, int w, int lane, Side &&side) {
+    const int lr = lane & 15, lg = lane >> 4;
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    if (w >= 4) side();   // waves past the fourth: independent work, if any
+    if (w < 4) {
+        const int b0 = 16 * w;
+        float *s0 = scr + w * 640, *s1 = s0 + 320;
+        const auto N = [&](int r, int c) { return Am[b0 + r][b0 + c]; };
+        const f32x4 p1 = mm16(N, N, z, lr, lg);               // N^2
+        scr_put(s0, p1, lr, lg);
+        const f32x4 p2 = mm16(scr_at(s0), scr_at(s0), z, lr, lg);   // N^4
+        const f32x4 y = mm16(N, scr_at(s0), z, lr, lg);       // N^3
+        f32x4 x;                                               // (I - N)(I + N^2)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = 4 * lg + r;
+            x[r] = (row == lr ? 1.f : 0.f) - Am[b0 + row][b0 + lr] + p1[r] - y[r];
+        }
+        scr_put(s0, p2, lr, lg);                               // (this wave's reads of N^2 came first)
+        scr_put(s1, x, lr, lg);
+        const f32x4 p3 = mm16(scr_at(s0), scr_at(s0), z, lr, lg);   // N^8
+        x = mm16(scr_at(s1), scr_at(s0), x, lr, lg);           // X (I + N^4)
+        scr_put(s0, p3, lr, lg);
+        scr_put(s1, x, lr, lg);
+        x = mm16(scr_at(s1), scr_at(s0), x, lr, lg);           // X (I + N^8)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Tm[b0 + 4 * lg + r][b0 + lr] = x[r];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int d = 1; d <= 3; ++d) {
+        if (w < 4 - d) {
+            const int j = w, i = j + d;
+            float *s0 = scr + w * 640;
+            f32x4 y = z;
+            for (int m = j; m < i; ++m)
+                y = mm16([&](int r, int c) { return Am[16 * i + r][16 * m + c]; },
+                         [&](int r, int c) { return Tm[16 * m + r][16 * j + c]; }, y, lr, lg);
+            scr_put(s0, y, lr, lg);
+            const f32x4 x = mm16([&](int r, int c) { return Tm[16 * i + r][16 * i + c]; }, scr_at(s0), z, lr, lg);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Tm[16 * i + 4 * lg + r][16 * j + lr] = -x[r];
+        }
+        __syncthreads();
+    }
+}
+
+// Gram matrices and Linv of the staged chunk (all NWS >= 4 waves; barriers
+// inside).  On entry Ks, Qs and the gates are in LDS; on exit Pm and Tm hold P
+// and Linv in their lower block triangles (diagonal blocks included, zero above
+// the diagonal within them); the strictly upper blocks are never written.  scr:
+// 10 KiB of LDS for the inverse, free until the chunk's products; `side` runs on
+// waves past the fourth during the inverse, after the Gram matrices.
+template <int DK, int NWS, typename SM, typename Side>
+__device__ inline void chunk_prep(SM &sm, int tid, int w, int lane, float *scr, Side &&side) {
     constexpr int KB = DK / 32;
     constexpr int NT = 64 * NWS;
     const int lr = lane & 15, lg = lane >> 4;
@@ -208,47 +294,7 @@ __device__ inline void chunk_prep(SM &sm, int tid, int w, int lane) {
         }
     }
     __syncthreads();
-    // Linv = (I + A)^{-1} by 16x16 blocks.  Diagonal blocks by forward
-    // substitution, lane = (block lg, column lr).
-    if (w == 0) {
-        const int base = 16 * lg;
-        float x[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float acc = r == lr ? 1.f : 0.f;
-#pragma unroll
-            for (int jj = 0; jj < r; ++jj) acc -= sm.Am[base + r][base + jj] * x[jj];
-            x[r] = acc;
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sm.Tm[base + r][base + lr] = x[r];
-    }
-    __syncthreads();
-    // Off-diagonal blocks, one block diagonal at a time:
-    //   X_ij = -X_ii sum_{m=j}^{i-1} A_im X_mj   (i = j + d).
-    for (int d = 1; d <= 3; ++d) {
-        const int npairs = 4 - d;
-        for (int idx = tid; idx < npairs * 256; idx += NT) {
-            const int j = idx >> 8, r = (idx >> 4) & 15, cc = idx & 15;
-            const int i = j + d;
-            float acc = 0.f;
-            for (int mb = j; mb < i; ++mb)
-#pragma unroll
-                for (int m = 0; m < 16; ++m)
-                    acc += sm.Am[16 * i + r][16 * mb + m] * sm.Tm[16 * mb + m][16 * j + cc];
-            sm.Wb[j][r][cc] = acc;
-        }
-        __syncthreads();
-        for (int idx = tid; idx < npairs * 256; idx += NT) {
-            const int j = idx >> 8, r = (idx >> 4) & 15, cc = idx & 15;
-            const int i = j + d;
-            float acc = 0.f;
-#pragma unroll
-            for (int m = 0; m < 16; ++m) acc += sm.Tm[16 * i + r][16 * i + m] * sm.Wb[j][m][cc];
-            sm.Tm[16 * i + r][16 * j + cc] = -acc;
-        }
-        __syncthreads();
-    }
+    tri_inverse(sm.Am, sm.Tm, scr, w, lane, side);
 }
 
 // Eight elements (row t, columns j8 .. j8 + 7) of Linv and of P, split into bf16
@@ -269,19 +315,24 @@ __device__ inline void split_mats8(const SM &sm, int t, int j8, Split8 &ls, Spli
     ps = split8(p8);
 }
 
-// The state-coupled products' A operands in LDS: Linv and P split.
-template <int DK, int NT>
-__device__ inline void split_mats(Smem<DK> &sm, int tid) {
-    for (int idx = tid; idx < C * C / 8; idx += NT) {
+// The state-coupled products' A operands in LDS: Linv (kP false) or P (kP true)
+// split, by threads t0, t0 + nt, ...; zero in the strictly upper blocks.
+template <bool kP, int DK>
+__device__ inline void split_mat(Smem<DK> &sm, int t0, int nt) {
+    for (int idx = t0; idx < C * C / 8; idx += nt) {
         const int t = idx / (C / 8), j8 = (idx - t * (C / 8)) * 8;
-        Split8 ls, ps;
-        split_mats8(sm, t, j8, ls, ps);
-        *reinterpret_cast<bf16x8 *>(&sm.LiH[t][j8]) = ls.hi;
-        *reinterpret_cast<bf16x8 *>(&sm.LiL[t][j8]) = ls.lo;
-        *reinterpret_cast<bf16x8 *>(&sm.PH[t][j8]) = ps.hi;
-        *reinterpret_cast<bf16x8 *>(&sm.PL[t][j8]) = ps.lo;
+        float a[8];
+        const float *src = kP ? &sm.Pm[t][j8] : &sm.Tm[t][j8];
+        *reinterpret_cast<float4 *>(a) = *reinterpret_cast<const float4 *>(src);
+        *reinterpret_cast<float4 *>(a + 4) = *reinterpret_cast<const float4 *>(src + 4);
+        if ((j8 >> 4) > (t >> 4)) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) a[e] = 0.f;
+        }
+        const Split8 sp = split8(a);
+        *reinterpret_cast<bf16x8 *>(kP ? &sm.PH[t][j8] : &sm.LiH[t][j8]) = sp.hi;
+        *reinterpret_cast<bf16x8 *>(kP ? &sm.PL[t][j8] : &sm.LiL[t][j8]) = sp.lo;
     }
-    __syncthreads();
 }
 
 // Scheduling fences between the steps of chunk_state (compiler-only; no
@@ -456,15 +507,6 @@ struct ChunkV {
     }
 };
 
-template <int DK>
-__device__ inline void clear_mats(Smem<DK> &sm, int tid, int nt) {
-    for (int idx = tid; idx < C * (C + 4); idx += nt) {
-        (&sm.Am[0][0])[idx] = 0.f;
-        (&sm.Tm[0][0])[idx] = 0.f;
-        (&sm.Pm[0][0])[idx] = 0.f;
-    }
-}
-
 // ---------------------------------------------------------------------------
 // One pass: one workgroup per (instance, head), NWS waves of 16 value rows.
 // ---------------------------------------------------------------------------
@@ -488,7 +530,6 @@ __global__ __launch_bounds__(64 * NWS) void prefill_kernel(
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 15, lg = lane >> 4;
     const int irow = slice * RS + w * 16 + lr;  // value row of this lane's column
-    clear_mats(sm, tid, NT);
 
     // State slice in registers: st[kt][r] = S[irow][16 kt + 4 lg + r].
     float *Srow = S + (size_t(bh) * DV + irow) * DK;
@@ -516,8 +557,11 @@ __global__ __launch_bounds__(64 * NWS) void prefill_kernel(
             if (w == 0) chunk_gates(sm, gt, bt, n, lane);
         }
         __syncthreads();
-        chunk_prep<DK, NWS>(sm, tid, w, lane);
-        split_mats<DK, NT>(sm, tid);
+        // The inverse's scratch: the split operands' space, rewritten below.
+        chunk_prep<DK, NWS>(sm, tid, w, lane, reinterpret_cast<float *>(&sm.LiH[0][0]), [] {});
+        split_mat<true>(sm, tid, NT);
+        split_mat<false>(sm, tid, NT);
+        __syncthreads();
         ChunkV cv;
         cv.load(v, row0, n, H, h, DV, irow, lg);
         float vv[4][4];
@@ -556,7 +600,7 @@ __device__ __forceinline__ void prep_unit(PrepSmem<DK> &sm, const __hip_bfloat16
         if (w == 0) chunk_gates(sm, gt, bt, n, lane);
     }
     __syncthreads();
-    chunk_prep<DK, NWS>(sm, tid, w, lane);
+    chunk_prep<DK, NWS>(sm, tid, w, lane, sm.Inv, [] {});
     // Linv hi, Linv lo, P hi, P lo as dense bf16 [C][C], then gam, ee, bet.
     uint8_t *out = ws + (size_t(bh) * nchunks + c) * kPrepBytes;
     for (int idx = tid; idx < C * C / 8; idx += NT) {
