@@ -1143,7 +1143,7 @@ hipError_t launch_dk_dv(float *S, const void *q, const void *k, const void *v, c
         // keeps pace with the scan chunk for chunk, so the segments are equal.
         // Short prompts, or a scan that leaves too few units idle, use one
         // segment (prep, then scan).
-        constexpr int kSeg = 3;
+        constexpr int kSeg = 4;
         int bnd[kSeg + 2], nseg = 1;
         bnd[0] = 0;
         bnd[1] = nchunks;
