@@ -204,9 +204,10 @@ __device__ inline auto scr_at(const float *m) {
 // Diagonal 16x16 blocks: with N strictly lower, N^16 = 0 and
 //   (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8),
 // three squarings and three products, one wave per block, its intermediates in
-// its own two scratch matrices (scr: 4 x 2 x 320 floats).  Off-diagonal blocks,
-// one block diagonal d at a time (block row i = j + d):
-//   X_ij = -X_ii sum_{m=j}^{i-1} A_im X_mj.
+// its own two scratch matrices (scr: 4 x 2 x 320 floats).  Off-diagonal blocks
+// by 2x2 blocking: X_10 = -X_11 A_10 X_00 and X_32 = -X_33 A_32 X_22 complete the
+// inverses X_A, X_B of the two 32x32 diagonal blocks, and the lower-left 32x32
+// block is -X_B A_BA X_A.
 // Every product of lower-triangular factors keeps exact zeros above the
 // diagonal and ones on it, so the diagonal blocks need no masking.
 template <typename MA, typename MT, typename Side>
@@ -239,22 +240,37 @@ __device__ inline void tri_inverse(const MA &Am, MT &Tm, float *scr, int w, int 
         for (int r = 0; r < 4; ++r) Tm[b0 + 4 * lg + r][b0 + lr] = x[r];
     }
     __syncthreads();
+    const auto A = [&](int bi, int bj) { return [&Am, bi, bj](int r, int c) { return Am[16 * bi + r][16 * bj + c]; }; };
+    const auto X = [&](int bi, int bj) { return [&Tm, bi, bj](int r, int c) { return Tm[16 * bi + r][16 * bj + c]; }; };
+    // The off-diagonal block inside each 32x32 diagonal block: X_10 and X_32.
+    if (w < 2) {
+        const int j = 2 * w, i = j + 1;
+        float *s0 = scr + w * 640;
+        scr_put(s0, mm16(A(i, j), X(j, j), z, lr, lg), lr, lg);
+        const f32x4 x = mm16(X(i, i), scr_at(s0), z, lr, lg);
 #pragma unroll
-    for (int d = 1; d <= 3; ++d) {
-        if (w < 4 - d) {
-            const int j = w, i = j + d;
-            float *s0 = scr + w * 640;
-            f32x4 y = z;
-            for (int m = j; m < i; ++m)
-                y = mm16([&](int r, int c) { return Am[16 * i + r][16 * m + c]; },
-                         [&](int r, int c) { return Tm[16 * m + r][16 * j + c]; }, y, lr, lg);
-            scr_put(s0, y, lr, lg);
-            const f32x4 x = mm16([&](int r, int c) { return Tm[16 * i + r][16 * i + c]; }, scr_at(s0), z, lr, lg);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Tm[16 * i + 4 * lg + r][16 * j + lr] = -x[r];
-        }
-        __syncthreads();
+        for (int r = 0; r < 4; ++r) Tm[16 * i + 4 * lg + r][16 * j + lr] = -x[r];
     }
+    __syncthreads();
+    // The lower-left 32x32 block: with X_A, X_B the inverses of the two diagonal
+    // 32x32 blocks and A_BA the lower-left block of A, it is -X_B (A_BA X_A).
+    // Y = A_BA X_A, block (p, q) on wave 2 (p - 2) + q ...
+    if (w < 4) {
+        const int p = 2 + (w >> 1), q = w & 1;
+        f32x4 y = mm16(A(p, 1), X(1, q), z, lr, lg);
+        if (q == 0) y = mm16(A(p, 0), X(0, 0), y, lr, lg);
+        scr_put(scr + w * 640, y, lr, lg);
+    }
+    __syncthreads();
+    // ... then X_ij = -sum_{m=2}^{i} X_im Y_mj, block (i, j) on wave 2 (i - 2) + j.
+    if (w < 4) {
+        const int i = 2 + (w >> 1), j = w & 1;
+        f32x4 x = mm16(X(i, 2), scr_at(scr + j * 640), z, lr, lg);
+        if (i == 3) x = mm16(X(3, 3), scr_at(scr + (2 + j) * 640), x, lr, lg);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Tm[16 * i + 4 * lg + r][16 * j + lr] = -x[r];
+    }
+    __syncthreads();
 }
 
 // Gram matrices and Linv of the staged chunk (all NWS >= 4 waves; barriers
