@@ -155,8 +155,8 @@ __global__ __launch_bounds__(256) void attn_split_kernel(
                 ks = k_new + o;
                 vs = v_new + o;
             }
-            dma16(ks, lk + 1024 * u);
-            dma16(vs, lv + 1024 * u);
+            dma16_nt(ks, lk + 1024 * u);
+            dma16_nt(vs, lv + 1024 * u);
         }
     };
 

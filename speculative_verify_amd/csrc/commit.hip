@@ -79,7 +79,7 @@ __global__ __launch_bounds__(kThreads) void commit_kernel(float *__restrict__ S,
         const int c4 = tid % F4_ROW, r0 = NP * (tid / F4_ROW);
         float4 s[NP];
 #pragma unroll
-        for (int p = 0; p < NP; ++p) s[p] = Sh[(r0 + p) * F4_ROW + c4];
+        for (int p = 0; p < NP; ++p) s[p] = ld_stream(reinterpret_cast<const float *>(Sh + (r0 + p) * F4_ROW + c4));
 
         const float *G = reinterpret_cast<const float *>(rec + RL.G);
         const float *D = reinterpret_cast<const float *>(rec + RL.delta);
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(kThreads) void commit_kernel(float *__restrict__ S,
             }
         }
 #pragma unroll
-        for (int p = 0; p < NP; ++p) Sh[(r0 + p) * F4_ROW + c4] = a[p];
+        for (int p = 0; p < NP; ++p) st_stream(reinterpret_cast<float *>(Sh + (r0 + p) * F4_ROW + c4), a[p]);
     }
 
     // Retire this workgroup's share of the block (every wave has read the flag

@@ -70,6 +70,17 @@ inline int esize_of(gdn_in_dtype dt) { return dt == GDN_IN_BF16 ? 2 : 4; }
 // ---------------------------------------------------------------------------
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// Streaming (non-temporal) 16-byte accesses for the recurrent state, which each
+// pass reads once and writes once: they should not displace reused data from
+// the caches, and they reach a higher HBM rate than plain accesses.
+__device__ inline float4 ld_stream(const float *p) {
+    const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ inline void st_stream(float *p, const float4 &v) {
+    __builtin_nontemporal_store(f32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4 *>(p));
+}
+
 __device__ inline float bf16_bits_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -149,6 +160,12 @@ __device__ inline void dma4(const void *src, uint32_t lds_base) {
 
 // The same with a uniform 64-bit base in SGPRs and a 32-bit per-lane byte
 // offset (the saddr form): no per-lane 64-bit address arithmetic.
+// dma16 for data read once (a streaming, non-temporal load).
+__device__ inline void dma16_nt(const void *src, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(__builtin_amdgcn_readfirstlane(lds_base)),
+                 "v"(src)
+                 : "memory", "m0");
+}
 __device__ inline void dma16s(const void *sbase, uint32_t voff, uint32_t lds_base) {
     // Both are wave-uniform by contract; readfirstlane keeps them in SGPRs where
     // the compiler cannot prove it (free when they already are).

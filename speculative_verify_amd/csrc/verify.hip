@@ -377,7 +377,7 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void ve
     auto load_tile = [&](int nt) {
 #pragma unroll
         for (int m = 0; m < KM; ++m)
-            sreg[nt][m] = *reinterpret_cast<const float4 *>(Sw + size_t(16 * nt) * DK + 16 * m);
+            sreg[nt][m] = ld_stream(Sw + size_t(16 * nt) * DK + 16 * m);
     };
 #pragma unroll
     for (int nt = 0; nt < NPRE; ++nt) load_tile(nt);
@@ -646,7 +646,7 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void ve
                 }
                 float *Sw_out = S + (size_t(bh) * DV + row) * DK + 4 * lg;
 #pragma unroll
-                for (int m = 0; m < KM; ++m) *reinterpret_cast<float4 *>(Sw_out + 16 * m) = sreg[nt][m];
+                for (int m = 0; m < KM; ++m) st_stream(Sw_out + 16 * m, sreg[nt][m]);
             }
             if (nt + NPRE < NT) load_tile(nt + NPRE);
         } else if constexpr (MIX) {
@@ -716,11 +716,18 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void ve
 #pragma unroll
                 for (int j = 0; j <= t; ++j) ot += coefN[t][j] * d[j];
                 const size_t idx = (size_t(b * T + t) * H + h) * DV + i;
+                // Streaming stores help the plain verify and cost the fused kernel
+                // (measured), whose state write-backs are streaming already.
                 if constexpr (MIX)
                     oo[t] = ot;
-                else
+                else if constexpr (FUSED)
                     o[idx] = ot;
-                Drec[idx] = dt;
+                else
+                    __builtin_nontemporal_store(ot, o + idx);
+                if constexpr (FUSED)
+                    Drec[idx] = dt;
+                else
+                    __builtin_nontemporal_store(dt, Drec + idx);
             }
         }
     }
