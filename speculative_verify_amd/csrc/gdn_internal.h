@@ -80,6 +80,11 @@ __device__ inline float4 ld_stream(const float *p) {
 __device__ inline void st_stream(float *p, const float4 &v) {
     __builtin_nontemporal_store(f32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4 *>(p));
 }
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ inline uint4 ld_stream_u4(const void *p) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 __device__ inline float bf16_bits_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
 

@@ -120,6 +120,9 @@ struct ChunkKQ {
     uint4 kv[NLD], qv[NLD];
     // Rows past the prompt read the last valid row (always a valid address); they
     // are zeroed when stored, never here, so nothing waits on these loads early.
+    // kStream: streaming loads, for rows nothing reads again soon (the one-pass
+    // kernel; the two-phase prep's rows are read again by the scan).
+    template <bool kStream = false>
     __device__ inline void load(const __hip_bfloat16 *k, const __hip_bfloat16 *q, size_t row0, int n,
                                 int H, int h, int tid) {
 #pragma unroll
@@ -127,8 +130,8 @@ struct ChunkKQ {
             const int idx = tid + u * NT;
             const int t = idx / (DK / 8), col = (idx - t * (DK / 8)) * 8;
             const size_t off = ((row0 + min(t, n - 1)) * H + h) * DK + col;
-            kv[u] = *reinterpret_cast<const uint4 *>(k + off);
-            qv[u] = *reinterpret_cast<const uint4 *>(q + off);
+            kv[u] = kStream ? ld_stream_u4(k + off) : *reinterpret_cast<const uint4 *>(k + off);
+            qv[u] = kStream ? ld_stream_u4(q + off) : *reinterpret_cast<const uint4 *>(q + off);
         }
     }
     // kTrans: also write the transposed keys (the state update's A operand).
@@ -473,7 +476,7 @@ __device__ inline void chunk_state(const Smem<DK> &sm, float (&st)[DK / 16][4], 
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int tr = 16 * tt + 4 * lg + r;
-            if (tr < n) obase[size_t(tr) * ostride] = Ot[r];
+            if (tr < n) __builtin_nontemporal_store(Ot[r], obase + size_t(tr) * ostride);
         }
         sched_fence<F>();
     }
@@ -509,7 +512,7 @@ struct ChunkV {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 16 * tt + 4 * lg + r;
-                raw[tt][r] = vb[((row0 + min(t, n - 1)) * H + h) * DV + irow];
+                raw[tt][r] = __builtin_nontemporal_load(vb + ((row0 + min(t, n - 1)) * H + h) * DV + irow);
             }
     }
     __device__ inline void get(float (&vv)[4][4], int n, int lg) const {
@@ -566,7 +569,7 @@ __global__ __launch_bounds__(64 * NWS) void prefill_kernel(
         const size_t row0 = size_t(b) * L + c0;  // (b, c0) token row
         {
             ChunkKQ<DK, NT> kq;
-            kq.load(k, q, row0, n, H, h, tid);
+            kq.template load<true>(k, q, row0, n, H, h, tid);
             const size_t gi = (row0 + min(lane, n - 1)) * H + h;
             const float gt = g[gi], bt = beta[gi];
             kq.store(sm, n, tid);
@@ -723,7 +726,7 @@ __device__ inline void scan_store_o(const ScanLds<DK> &sm, int n, int lane, int 
         const int row = 32 * (j >> 4) + 8 * ((j >> 2) & 3) + 4 * kh + (j & 3);
         const int col = 16 * g + 4 * (lane & 3);
         const float4 v4 = *reinterpret_cast<const float4 *>(&sm.O[row * kOStride + col]);
-        if (row < n) *reinterpret_cast<float4 *>(obase + size_t(row) * ostride + col) = v4;
+        if (row < n) st_stream(obase + size_t(row) * ostride + col, v4);
     }
 }
 
