@@ -109,21 +109,23 @@ __device__ inline float softplusf(float x) { return x > 20.f ? x : log1pf(expf(x
 __device__ inline uint32_t ldbits(const __hip_bfloat16 *p, size_t i) {
     return reinterpret_cast<const uint16_t *>(p)[i];
 }
-// Sum over the wave, returned (uniform) to every lane: DPP within each row of 16
-// lanes (swap neighbours, swap pairs, mirror within 8, mirror within 16: every
-// lane then holds its row's sum), then the four row sums read out as scalars.
-// No LDS round trips, unlike a shuffle tree.
-template <int CTRL> __device__ inline float dpp_add(float v) {
-    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+// Sum over the wave, returned (uniform) to every lane, all in DPP: within each
+// row of 16 lanes swap neighbours, swap pairs, mirror within 8 and within 16
+// (every lane then holds its row's sum); then lane 15 of rows 0 and 2 is added
+// into rows 1 and 3 (row_bcast:15), and lane 31 into rows 2 and 3
+// (row_bcast:31), so lane 63 holds the total, read out once.  No LDS round trips,
+// unlike a shuffle tree.
+template <int CTRL, int ROWS = 0xf> __device__ inline float dpp_add(float v) {
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xf, false));
 }
 __device__ inline float wave_sum(float v) {
-    v = dpp_add<0xB1>(v);    // quad_perm [1,0,3,2]
-    v = dpp_add<0x4E>(v);    // quad_perm [2,3,0,1]
-    v = dpp_add<0x141>(v);   // row_half_mirror
-    v = dpp_add<0x140>(v);   // row_mirror
-    const int u = __float_as_int(v);
-    return (__int_as_float(__builtin_amdgcn_readlane(u, 0)) + __int_as_float(__builtin_amdgcn_readlane(u, 16))) +
-           (__int_as_float(__builtin_amdgcn_readlane(u, 32)) + __int_as_float(__builtin_amdgcn_readlane(u, 48)));
+    v = dpp_add<0xB1>(v);          // quad_perm [1,0,3,2]
+    v = dpp_add<0x4E>(v);          // quad_perm [2,3,0,1]
+    v = dpp_add<0x141>(v);         // row_half_mirror
+    v = dpp_add<0x140>(v);         // row_mirror
+    v = dpp_add<0x142, 0xa>(v);    // row_bcast:15 into rows 1 and 3
+    v = dpp_add<0x143, 0xc>(v);    // row_bcast:31 into rows 2 and 3
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 // X rows: 0..TM-1 hold k_1..k_TM, TM..2TM-1 hold q_1..q_TM (TM = 8 MT); rows of
