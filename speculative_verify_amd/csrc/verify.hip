@@ -374,6 +374,7 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void ve
     //    reads and write-backs share the memory system instead of queueing as a
     //    read phase followed by a write phase.
     constexpr int NPRE = (FUSED || MIX) ? (NT < 2 ? NT : 2) : NT;   // tiles loaded up front
+    constexpr int NEARLY = FUSED ? (NPRE < 1 ? NPRE : 1) : 0;          // tiles committed before the Gram
     const float *Sw = S + (size_t(bh) * DV + rbase + RW * w + lr) * DK + 4 * lg;
     float4 sreg[NT][KM];
     auto load_tile = [&](int nt) {
@@ -482,6 +483,84 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void ve
             }
         }
     }
+    // FUSED: the commit of state tile nt (in registers), its write-back, and the
+    // load of the tile NPRE ahead.  Needs only the pending block's rows, so the
+    // first NEARLY tiles are committed before this block's Gram matrix and
+    // coefficients, and the state keeps streaming meanwhile.
+    auto commit_tile = [&](int nt) {
+        if (cn > 0) {
+            // S_n = exp(G_n) S + sum_{j < n} exp(G_n - G_j) delta_j k_j^T for this
+            // tile (row 64w + 16nt + lr, keys 16m + 4lg + {0..3}), written back.
+            const int row = rbase + RW * w + 16 * nt + lr;
+#pragma unroll
+            for (int m = 0; m < KM; ++m) {
+                sreg[nt][m].x *= gam_n;
+                sreg[nt][m].y *= gam_n;
+                sreg[nt][m].z *= gam_n;
+                sreg[nt][m].w *= gam_n;
+            }
+            auto add_row = [&](float c, const float4 (&kv)[KM]) {
+#pragma unroll
+                for (int m = 0; m < KM; ++m) {
+                    sreg[nt][m].x += c * kv[m].x;
+                    sreg[nt][m].y += c * kv[m].y;
+                    sreg[nt][m].z += c * kv[m].z;
+                    sreg[nt][m].w += c * kv[m].w;
+                }
+            };
+            const int nr = min(cn, CR);
+            if (esp == 2) {
+#pragma unroll 1
+                for (int j = 0; j < nr; ++j) {
+                    float4 kv[KM];
+#pragma unroll
+                    for (int m = 0; m < KM; ++m) {
+                        const uint2 r2 = *reinterpret_cast<const uint2 *>(kraw + (j * DK + 16 * m + 4 * lg) * 2);
+                        kv[m] = make_float4(__uint_as_float(r2.x << 16), __uint_as_float(r2.x & 0xffff0000u),
+                                            __uint_as_float(r2.y << 16), __uint_as_float(r2.y & 0xffff0000u));
+                    }
+                    add_row(cdraw[j * DV + row], kv);
+                }
+            } else {
+#pragma unroll 1
+                for (int j = 0; j < nr; ++j) {
+                    float4 kv[KM];
+#pragma unroll
+                    for (int m = 0; m < KM; ++m)
+                        kv[m] = *reinterpret_cast<const float4 *>(kraw + (j * DK + 16 * m + 4 * lg) * 4);
+                    add_row(cdraw[j * DV + row], kv);
+                }
+            }
+            // Rows past CR (blocks longer than 8): straight from the record.
+#pragma unroll 1
+            for (int j = CR; j < cn; ++j) {
+                const size_t rj = (size_t(b) * Tp + j) * H + h;
+                const float c = expf(gprev[cn - 1] - reinterpret_cast<const float *>(rprev + RLp.G)[rj]) *
+                                reinterpret_cast<const float *>(rprev + RLp.delta)[rj * DV + row];
+                float4 kv[KM];
+#pragma unroll
+                for (int m = 0; m < KM; ++m) {
+                    const int key = 16 * m + 4 * lg;
+                    if (esp == 2) {
+                        const uint2 r2 = *reinterpret_cast<const uint2 *>(rprev + RLp.kcopy + (rj * DK + key) * 2);
+                        kv[m] = make_float4(__uint_as_float(r2.x << 16), __uint_as_float(r2.x & 0xffff0000u),
+                                            __uint_as_float(r2.y << 16), __uint_as_float(r2.y & 0xffff0000u));
+                    } else {
+                        kv[m] = *reinterpret_cast<const float4 *>(rprev + RLp.kcopy + (rj * DK + key) * 4);
+                    }
+                }
+                add_row(c, kv);
+            }
+            float *Sw_out = S + (size_t(bh) * DV + row) * DK + 4 * lg;
+#pragma unroll
+            for (int m = 0; m < KM; ++m) st_stream(Sw_out + 16 * m, sreg[nt][m]);
+        }
+        if (nt + NPRE < NT) load_tile(nt + NPRE);
+    };
+    if constexpr (FUSED) {
+#pragma unroll
+        for (int nt = 0; nt < NEARLY; ++nt) commit_tile(nt);
+    }
     if (w == 0) {
         // Log-decay prefix sums over the block, in one fixed order (a wave scan);
         // the commit reuses the stored values.  Read by the coefficients after
@@ -583,74 +662,7 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void ve
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         if constexpr (FUSED) {
-            if (cn > 0) {
-                // S_n = exp(G_n) S + sum_{j < n} exp(G_n - G_j) delta_j k_j^T for this
-                // tile (row 64w + 16nt + lr, keys 16m + 4lg + {0..3}), written back.
-                const int row = rbase + RW * w + 16 * nt + lr;
-#pragma unroll
-                for (int m = 0; m < KM; ++m) {
-                    sreg[nt][m].x *= gam_n;
-                    sreg[nt][m].y *= gam_n;
-                    sreg[nt][m].z *= gam_n;
-                    sreg[nt][m].w *= gam_n;
-                }
-                auto add_row = [&](float c, const float4 (&kv)[KM]) {
-#pragma unroll
-                    for (int m = 0; m < KM; ++m) {
-                        sreg[nt][m].x += c * kv[m].x;
-                        sreg[nt][m].y += c * kv[m].y;
-                        sreg[nt][m].z += c * kv[m].z;
-                        sreg[nt][m].w += c * kv[m].w;
-                    }
-                };
-                const int nr = min(cn, CR);
-                if (esp == 2) {
-#pragma unroll 1
-                    for (int j = 0; j < nr; ++j) {
-                        float4 kv[KM];
-#pragma unroll
-                        for (int m = 0; m < KM; ++m) {
-                            const uint2 r2 = *reinterpret_cast<const uint2 *>(kraw + (j * DK + 16 * m + 4 * lg) * 2);
-                            kv[m] = make_float4(__uint_as_float(r2.x << 16), __uint_as_float(r2.x & 0xffff0000u),
-                                                __uint_as_float(r2.y << 16), __uint_as_float(r2.y & 0xffff0000u));
-                        }
-                        add_row(cdraw[j * DV + row], kv);
-                    }
-                } else {
-#pragma unroll 1
-                    for (int j = 0; j < nr; ++j) {
-                        float4 kv[KM];
-#pragma unroll
-                        for (int m = 0; m < KM; ++m)
-                            kv[m] = *reinterpret_cast<const float4 *>(kraw + (j * DK + 16 * m + 4 * lg) * 4);
-                        add_row(cdraw[j * DV + row], kv);
-                    }
-                }
-                // Rows past CR (blocks longer than 8): straight from the record.
-#pragma unroll 1
-                for (int j = CR; j < cn; ++j) {
-                    const size_t rj = (size_t(b) * Tp + j) * H + h;
-                    const float c = expf(gprev[cn - 1] - reinterpret_cast<const float *>(rprev + RLp.G)[rj]) *
-                                    reinterpret_cast<const float *>(rprev + RLp.delta)[rj * DV + row];
-                    float4 kv[KM];
-#pragma unroll
-                    for (int m = 0; m < KM; ++m) {
-                        const int key = 16 * m + 4 * lg;
-                        if (esp == 2) {
-                            const uint2 r2 = *reinterpret_cast<const uint2 *>(rprev + RLp.kcopy + (rj * DK + key) * 2);
-                            kv[m] = make_float4(__uint_as_float(r2.x << 16), __uint_as_float(r2.x & 0xffff0000u),
-                                                __uint_as_float(r2.y << 16), __uint_as_float(r2.y & 0xffff0000u));
-                        } else {
-                            kv[m] = *reinterpret_cast<const float4 *>(rprev + RLp.kcopy + (rj * DK + key) * 4);
-                        }
-                    }
-                    add_row(c, kv);
-                }
-                float *Sw_out = S + (size_t(bh) * DV + row) * DK + 4 * lg;
-#pragma unroll
-                for (int m = 0; m < KM; ++m) st_stream(Sw_out + 16 * m, sreg[nt][m]);
-            }
-            if (nt + NPRE < NT) load_tile(nt + NPRE);
+            if (nt >= NEARLY) commit_tile(nt);
         } else if constexpr (MIX) {
             if (nt + NPRE < NT) load_tile(nt + NPRE);
         }
