@@ -18,10 +18,11 @@
 // each:
 //   stats  (B x rows x slices): per slice, the argmax of the raw logits and, for
 //          sampled mode, max and sum of exp of logits / tau;
-//   decide (B, one wave): combine the slices of each row, walk the drafts in
-//          order, write n (and, greedy, the emitted token);
-//   mass   (B x slices, sampled): per slice, the mass of the weights the
-//          emitted token is drawn from;
+//   decide (B): combine the slices of each row, walk the drafts in order,
+//          write n and the emitted token (greedy);
+//   mass   (B x slices, sampled): every workgroup makes the sampled decision
+//          (the same in each), slice 0 writes n, then per slice the mass of
+//          the weights the emitted token is drawn from;
 //   pick   (B, sampled): find the slice, then the entry, where the cumulative
 //          weight passes u times the total.
 #include <climits>
@@ -144,14 +145,16 @@ __global__ __launch_bounds__(kThreads) void accept_stats_kernel(const TIn *__res
 
 constexpr int kPartChunk = 2048;   // (row, slice) statistics staged in LDS at a time
 
-// One workgroup per sequence: combine the slices of every row (all statistics
-// loaded at once into LDS, then one row per wave), then walk the drafts.
+// The decision for sequence b, by one whole workgroup: combine the slices of
+// every row (statistics staged in LDS, one row per wave), then walk the drafts.
+// Returns m (kept drafts) to every thread; for sampled mode *pk_out gets the
+// draw's description, and for greedy mode *greedy_next the emitted token.
 template <typename TIn, bool SAMPLED>
-__global__ __launch_bounds__(kThreads) void accept_decide_kernel(
-    const TIn *__restrict__ tgt, const TIn *__restrict__ drf, const int32_t *__restrict__ drafts,
-    const float *__restrict__ u_acc, int T, int V, int ns, float inv_tau, const Part *__restrict__ parts,
-    Pick *__restrict__ pick, int32_t *__restrict__ n_out, int32_t *__restrict__ next) {
-    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+__device__ __forceinline__ int decide_block(const TIn *__restrict__ tgt, const TIn *__restrict__ drf,
+                                            const int32_t *__restrict__ drafts, const float *__restrict__ u_acc,
+                                            int b, int T, int V, int ns, float inv_tau,
+                                            const Part *__restrict__ parts, Pick *pk_out, int *greedy_next) {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int rows = SAMPLED ? 2 * T - 1 : T;
     __shared__ Part stage[kPartChunk];
     __shared__ float M[2 * GDN_T_MAX], S[2 * GDN_T_MAX], BV[2 * GDN_T_MAX];
@@ -213,11 +216,11 @@ __global__ __launch_bounds__(kThreads) void accept_decide_kernel(
         }
     }
     __syncthreads();
-    if (tid != 0) return;
+    // The walk (cheap: at most T - 1 steps over LDS), by every thread alike.
     int m = 0;
     if constexpr (!SAMPLED) {
         while (m < T - 1 && D[m] == AM[m]) ++m;
-        next[b] = AM[m];
+        *greedy_next = AM[m];
     } else {
         while (m < T - 1) {
             const int d = D[m];
@@ -236,9 +239,26 @@ __global__ __launch_bounds__(kThreads) void accept_decide_kernel(
         pk.sd = pk.residual ? S[T + m] : 1.f;
         pk.amax = AM[m];
         pk.pad = 0;
-        pick[b] = pk;
+        *pk_out = pk;
     }
-    n_out[b] = m + 1;
+    __syncthreads();   // the staging buffers may be reused by the caller
+    return m;
+}
+
+// Greedy decision: one workgroup per sequence.
+template <typename TIn>
+__global__ __launch_bounds__(kThreads) void accept_decide_kernel(const TIn *__restrict__ tgt,
+                                                                 const int32_t *__restrict__ drafts, int T, int V,
+                                                                 int ns, const Part *__restrict__ parts,
+                                                                 int32_t *__restrict__ n_out,
+                                                                 int32_t *__restrict__ next) {
+    const int b = blockIdx.x;
+    int nx = 0;
+    const int m = decide_block<TIn, false>(tgt, nullptr, drafts, nullptr, b, T, V, ns, 1.f, parts, nullptr, &nx);
+    if (threadIdx.x == 0) {
+        next[b] = nx;
+        n_out[b] = m + 1;
+    }
 }
 
 // Weight of vocabulary entry i in the draw, p(i) or max(0, p(i) - q(i)) in
@@ -291,13 +311,26 @@ __device__ inline uint64_t block_excl_scan(uint64_t v, uint64_t *total) {
     return base + incl - v;
 }
 
+// Sampled decision and the draw's masses in one launch: every workgroup of a
+// sequence makes the same decision from the same statistics (deterministic, so
+// they agree), slice 0 publishes it, and each workgroup then weighs its slice
+// of the row the token is drawn from.  One launch instead of a decision launch
+// followed by a mass launch.
 template <typename TIn>
 __global__ __launch_bounds__(kThreads) void accept_mass_kernel(const TIn *__restrict__ tgt,
-                                                               const TIn *__restrict__ drf, int T, int V, int ns,
-                                                               float inv_tau, const Pick *__restrict__ pick,
+                                                               const TIn *__restrict__ drf,
+                                                               const int32_t *__restrict__ drafts,
+                                                               const float *__restrict__ u_acc, int T, int V, int ns,
+                                                               float inv_tau, const Part *__restrict__ parts,
+                                                               Pick *__restrict__ pick, int32_t *__restrict__ n_out,
                                                                uint64_t *__restrict__ mass) {
     const int s = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-    const Pick pk = pick[b];
+    Pick pk;
+    const int m = decide_block<TIn, true>(tgt, drf, drafts, u_acc, b, T, V, ns, inv_tau, parts, &pk, nullptr);
+    if (s == 0 && tid == 0) {
+        pick[b] = pk;
+        n_out[b] = m + 1;
+    }
     const TIn *trow = tgt + (size_t(b) * T + pk.row) * V;
     const TIn *drow = pk.residual ? drf + (size_t(b) * (T - 1) + pk.row) * V : nullptr;
     const int lo = s * kSlice, hi = min(V, lo + kSlice);
@@ -439,9 +472,8 @@ hipError_t accept_greedy_t(const TIn *tgt, const int32_t *drafts, int B, int T, 
                        static_cast<const TIn *>(nullptr), T, V, ns, 1.f, parts);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((accept_decide_kernel<TIn, false>), dim3(B), dim3(kThreads), 0, st, tgt,
-                       static_cast<const TIn *>(nullptr), drafts, static_cast<const float *>(nullptr), T, V, ns,
-                       1.f, parts, reinterpret_cast<Pick *>(ws + L.pick), n_out, next);
+    hipLaunchKernelGGL((accept_decide_kernel<TIn>), dim3(B), dim3(kThreads), 0, st, tgt, drafts, T, V, ns, parts,
+                       n_out, next);
     return hipGetLastError();
 }
 
@@ -458,11 +490,8 @@ hipError_t accept_sampled_t(const TIn *tgt, const TIn *drf, const int32_t *draft
                        V, ns, inv_tau, parts);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((accept_decide_kernel<TIn, true>), dim3(B), dim3(kThreads), 0, st, tgt, drf, drafts, u_acc, T, V,
-                       ns, inv_tau, parts, pick, n_out, static_cast<int32_t *>(nullptr));
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((accept_mass_kernel<TIn>), dim3(ns, B), dim3(kThreads), 0, st, tgt, drf, T, V, ns, inv_tau,
-                       pick, mass);
+    hipLaunchKernelGGL((accept_mass_kernel<TIn>), dim3(ns, B), dim3(kThreads), 0, st, tgt, drf, drafts, u_acc, T, V,
+                       ns, inv_tau, parts, pick, n_out, mass);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((accept_pick_kernel<TIn>), dim3(B), dim3(kThreads), 0, st, tgt, drf, T, V, ns, inv_tau,
                        pick, mass, u_samp, next);
