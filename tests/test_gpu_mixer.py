@@ -83,3 +83,36 @@ def test_mixer_commit_verify_two_blocks(G):
     S_ref = oracle.commit(S5, *qkv1, np.full(B, 3, np.int32))
     assert rel_err_outputs(y1, y1_ref) <= OUT_TOL
     assert rel_err_state(S, S_ref) <= STATE_TOL
+
+
+def test_mixer_48_layers_sampled(G):
+    """The benchmark's shape and launch: 48 layers x 32 value heads (16 q/k heads),
+    T = 8, a mixer verify, then a fused commit (n = 5) + mixer verify of the next
+    block.  Layers 0, 23 and 47 against the oracle computed for them alone."""
+    B, H, Hk, T = 48, 32, 16, 8
+    print_case(test="mixer_48_layers", B=B, H=H, Hk=Hk, T=T, seed=31)
+    S0 = make_inputs(B, H, D, D, 1, seed=31, device=DEV, device_gen=True).S0
+    full = make_mixer_inputs(B, 2 * T, H, Hk, D, seed=31, device=DEV)
+    m0, m1 = full.block(0, T), full.block(1, T)
+    S = S0.clone()
+    ra, rb = G.new_record(S, T, torch.bfloat16), G.new_record(S, T, torch.bfloat16)
+    y0 = torch.empty(B, T, H, D, device=DEV)
+    y1 = torch.empty(B, T, H, D, device=DEV)
+    G.gdn_mixer_verify(S, m0, y0, ra)
+    G.gdn_mixer_commit_verify(S, ra, torch.full((B,), 5, dtype=torch.int32, device=DEV), m1, y1, rb)
+    torch.cuda.synchronize()
+
+    def layer(m, b):
+        pick = lambda t: t[b:b + 1].contiguous()
+        return type(m)(pick(m.x), pick(m.history), m.conv_w, pick(m.a), pick(m.b), m.A_log, m.dt_bias,
+                       pick(m.z), m.norm_w, m.Hk).to("cpu")
+
+    for b in (0, 23, 47):
+        S0b = S0[b:b + 1].cpu().double().numpy()
+        y0_ref, qkv0 = ref_block(S0b, layer(m0, b), H)
+        S5 = oracle.commit(S0b, *qkv0, np.array([5], np.int32))
+        y1_ref, _ = ref_block(S5, layer(m1, b), H)
+        e0, e1 = rel_err_outputs(y0[b:b + 1], y0_ref), rel_err_outputs(y1[b:b + 1], y1_ref)
+        es = rel_err_state(S[b:b + 1], S5)
+        print(f"  layer {b}: out {e0:.2e} / {e1:.2e}, state {es:.2e}", flush=True)
+        assert e0 <= OUT_TOL and e1 <= OUT_TOL and es <= STATE_TOL
