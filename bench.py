@@ -428,6 +428,7 @@ def main():
     }
 
     result["copy_ceiling"] = copy_ceiling(dev)
+    result["copy_same_size"] = copy_same_size(dev, roof["algorithmic_bytes_per_launch"], roof["achieved"])
     if not args.no_prefill:
         result["prefill"] = bench_prefill(args, G, dev)
     if not args.no_prefill_long:
@@ -451,6 +452,35 @@ def main():
         torch.cuda.synchronize()
         result["copy_calibration"] = {"bytes_read": n * 4, "bytes_written": n * 4, "launches": 3}
     print(json.dumps(result), flush=True)
+
+
+def copy_same_size(dev, nbytes, pass_gbs, pairs=6, reps=30):
+    """Achieved GB/s of a device-to-device copy that moves as many bytes as one
+    launch of the headline pass (half read, half written), rotated over `pairs`
+    buffer pairs so that no copy finds its source in the 256 MB last-level cache.
+    A launch's ramp-up and drain weigh more at this size than at 1 GiB, so this
+    is the ceiling the pass itself runs against; `pass_vs_copy` is the pass's
+    rate over the copy's."""
+    import torch
+
+    n = max(1, nbytes // 8)  # fp32 elements per side
+    bufs = [(torch.ones(n, dtype=torch.float32, device=dev), torch.empty(n, dtype=torch.float32, device=dev))
+            for _ in range(pairs)]
+    for s_, d_ in bufs:
+        d_.copy_(s_)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(reps):
+        s_, d_ = bufs[i % pairs]
+        d_.copy_(s_)
+    b.record()
+    torch.cuda.synchronize()
+    gbs = 2 * n * 4 * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+    del bufs
+    torch.cuda.empty_cache()
+    return {"kernel": "torch copy_", "bytes_per_copy": 2 * n * 4, "pairs": pairs, "achieved": round(gbs, 1),
+            "unit": "GB/s", "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "pass_vs_copy": round(pass_gbs / gbs, 4)}
 
 
 def copy_ceiling(dev, mib=1024, reps=10):
