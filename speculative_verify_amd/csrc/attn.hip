@@ -134,11 +134,36 @@ __global__ __launch_bounds__(256) void attn_split_kernel(
         }
     }
     const int vis = qi < R ? ctx + qt : -1;  // last key position this row sees
+    const bool rows_full = (rg + 1) * kRows <= R;   // every query row of the workgroup is real
 
     // Copies of tile k0 into stage st: wave w issues copies u = w, w + 4, ...;
     // copy u fills LDS bytes 1024 u + 16 lane, row r, slot sl = piece ^ swz16(r).
+    // A tile of cached positions only (all but the split's last tile, as a rule)
+    // is copied from a uniform base with per-lane byte offsets that are the same
+    // for every tile and for keys and values; the other tiles take each row's
+    // source (cache, block row or clamp) lane by lane.
+    static_assert(NDMA % 4 == 0, "every wave issues the same number of copies");
+    constexpr int NCW = NDMA / 4;
+    uint32_t voff[NCW];
+#pragma unroll
+    for (int j = 0; j < NCW; ++j) {
+        const int byte = 1024 * (w + 4 * j) + 16 * lane;
+        const int r = byte / ROWB, sl = (byte - r * ROWB) >> 4;
+        voff[j] = uint32_t((size_t(r) * kv_row + 8 * (sl ^ swz16(r))) * 2);
+    }
+    const bool fast_ok = size_t(kTile) * kv_row * 2 < (size_t(1) << 31);   // offsets fit 32 bits
     auto issue = [&](int k0, int st) {
         const uint32_t lk = lds_addr(Ks[st]), lv = lds_addr(Vs[st]);
+        if (fast_ok && k0 + kTile <= ctx) {
+            const size_t o = (size_t(b) * Lmax + k0) * kv_row + size_t(g) * D;
+            const __hip_bfloat16 *kb = k_cache + o, *vb = v_cache + o;
+#pragma unroll
+            for (int j = 0; j < NCW; ++j) {
+                dma16s_nt(kb, voff[j], lk + 1024 * (w + 4 * j));
+                dma16s_nt(vb, voff[j], lv + 1024 * (w + 4 * j));
+            }
+            return;
+        }
 #pragma unroll
         for (int u = w; u < NDMA; u += 4) {
             const int byte = 1024 * u + 16 * lane;
@@ -176,6 +201,9 @@ __global__ __launch_bounds__(256) void attn_split_kernel(
         const uint8_t *Kc = Ks[st], *Vc = Vs[st];
 
         // S^T tiles: keys tau(kt, 4 lg + r) of this lane's query row, log2 domain.
+        // A tile of cached positions inside the split is visible to every query
+        // row of the workgroup (each sees all of the cache): no mask.
+        const bool unmasked = rows_full && k0 + kTile <= min(ctx, sr.end);
         float x[4][4];
         float mt = -INFINITY;
 #pragma unroll
@@ -184,12 +212,18 @@ __global__ __launch_bounds__(256) void attn_split_kernel(
             f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) s = mma(lds16(Kc + row_off<D>(r, 4 * kb + lg)), qf[kb], s);
+            if (unmasked) {
 #pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const int p = k0 + 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1) + r4;
-                x[kt][r4] = (p <= vis && p < sr.end) ? s[r4] * scale_log2 : -INFINITY;
-                mt = fmaxf(mt, x[kt][r4]);
+                for (int r4 = 0; r4 < 4; ++r4) x[kt][r4] = s[r4] * scale_log2;
+            } else {
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const int p = k0 + 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1) + r4;
+                    x[kt][r4] = (p <= vis && p < sr.end) ? s[r4] * scale_log2 : -INFINITY;
+                }
             }
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) mt = fmaxf(mt, x[kt][r4]);
         }
         mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
         mt = fmaxf(mt, __shfl_xor(mt, 32, 64));

@@ -185,6 +185,17 @@ __device__ inline void dma16s(const void *sbase, uint32_t voff, uint32_t lds_bas
                  : "memory", "m0");
 }
 
+// dma16s for data read once (a streaming, non-temporal load).
+__device__ inline void dma16s_nt(const void *sbase, uint32_t voff, uint32_t lds_base) {
+    const uint64_t sb = reinterpret_cast<uint64_t>(sbase);
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(sb >> 32)));
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(sb & 0xffffffffu)));
+    const uint64_t sbu = (uint64_t(hi) << 32) | uint64_t(lo);
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt" ::"s"(__builtin_amdgcn_readfirstlane(lds_base)),
+                 "v"(voff), "s"(sbu)
+                 : "memory", "m0");
+}
+
 __device__ inline uint32_t lds_addr(const void *p) {
     return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void *)p));
 }
