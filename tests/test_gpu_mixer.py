@@ -59,30 +59,33 @@ def test_mixer_verify_then_commit(G, B, H, Hk, T):
     assert eo <= OUT_TOL and es <= STATE_TOL
 
 
-def test_mixer_commit_verify_two_blocks(G):
+@pytest.mark.parametrize("T,n0,n1", [(8, 5, 3), (12, 10, 7), (16, 16, 9), (1, 1, 0)])
+def test_mixer_commit_verify_two_blocks(G, T, n0, n1):
     """Block 0 by gdn_mixer_verify, then block 1 by gdn_mixer_commit_verify at
-    n = 5: the outputs of block 1 come from S_5 of block 0, and a final commit
-    of block 1 at n = 3 lands on the oracle's state."""
-    B, H, Hk, T = 2, 8, 4, 8
-    print_case(test="mixer_commit_verify", B=B, H=H, Hk=Hk, T=T, seed=21)
-    S0 = make_inputs(B, H, D, D, 1, seed=21, device=DEV).S0
-    full = make_mixer_inputs(B, 2 * T, H, Hk, D, seed=21, device=DEV)
+    n = n0: the outputs of block 1 come from S_n0 of block 0, and a final commit
+    of block 1 at n = n1 lands on the oracle's state.  Blocks longer than 8 rows
+    replay their rows past the eighth straight from the record."""
+    B, H, Hk = 2, 8, 4
+    print_case(test="mixer_commit_verify", B=B, H=H, Hk=Hk, T=T, n0=n0, n1=n1, seed=21 + T)
+    S0 = make_inputs(B, H, D, D, 1, seed=21 + T, device=DEV).S0
+    full = make_mixer_inputs(B, 2 * T, H, Hk, D, seed=21 + T, device=DEV)
     m0, m1 = full.block(0, T), full.block(1, T)
     S = S0.clone()
     ra, rb = G.new_record(S, T, torch.bfloat16), G.new_record(S, T, torch.bfloat16)
     y0 = torch.empty(B, T, H, D, device=DEV)
     y1 = torch.empty(B, T, H, D, device=DEV)
     G.gdn_mixer_verify(S, m0, y0, ra)
-    G.gdn_mixer_commit_verify(S, ra, torch.full((B,), 5, dtype=torch.int32, device=DEV), m1, y1, rb)
-    G.gdn_commit(S, rb, torch.full((B,), 3, dtype=torch.int32, device=DEV))
+    G.gdn_mixer_commit_verify(S, ra, torch.full((B,), n0, dtype=torch.int32, device=DEV), m1, y1, rb)
+    G.gdn_commit(S, rb, torch.full((B,), n1, dtype=torch.int32, device=DEV))
     torch.cuda.synchronize()
     S0c = S0.cpu().double().numpy()
-    _, qkv0 = ref_block(S0c, m0.to("cpu"), H)
-    S5 = oracle.commit(S0c, *qkv0, np.full(B, 5, np.int32))
-    y1_ref, qkv1 = ref_block(S5, m1.to("cpu"), H)
-    S_ref = oracle.commit(S5, *qkv1, np.full(B, 3, np.int32))
-    assert rel_err_outputs(y1, y1_ref) <= OUT_TOL
-    assert rel_err_state(S, S_ref) <= STATE_TOL
+    y0_ref, qkv0 = ref_block(S0c, m0.to("cpu"), H)
+    Sn = oracle.commit(S0c, *qkv0, np.full(B, n0, np.int32))
+    y1_ref, qkv1 = ref_block(Sn, m1.to("cpu"), H)
+    S_ref = oracle.commit(Sn, *qkv1, np.full(B, n1, np.int32))
+    e0, e1, es = rel_err_outputs(y0, y0_ref), rel_err_outputs(y1, y1_ref), rel_err_state(S, S_ref)
+    print(f"  outputs {e0:.2e} / {e1:.2e}, state {es:.2e}", flush=True)
+    assert e0 <= OUT_TOL and e1 <= OUT_TOL and es <= STATE_TOL
 
 
 def test_mixer_48_layers_sampled(G):
