@@ -597,14 +597,15 @@ __global__ __launch_bounds__(64 * NWS) void prefill_kernel(
 
 // ---------------------------------------------------------------------------
 // Two-phase schedule, prep: a workgroup builds Linv, P and the gates of one
-// (instance, head, chunk) and writes them to that chunk's workspace record.
+// (instance, head, chunk) and writes them to that chunk's workspace record,
+// with NWS >= 4 waves.
 // ---------------------------------------------------------------------------
-template <int DK>
+template <int DK, int NWS>
 __device__ __forceinline__ void prep_unit(PrepSmem<DK> &sm, const __hip_bfloat16 *__restrict__ q,
                                  const __hip_bfloat16 *__restrict__ k, const float *__restrict__ g,
                                  const float *__restrict__ beta, int L, int H, int nchunks,
                                  uint8_t *__restrict__ ws, int bh, int c) {
-    constexpr int NWS = 4, NT = 256;
+    constexpr int NT = 64 * NWS;
     const int b = bh / H, h = bh - b * H;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1094,8 +1095,8 @@ union FusedLds {
 };
 
 // Prep records of chunks [pbeg, pend) for every (instance, head): unit u =
-// chunk-relative index * heads + head, workgroup u % nprep.
-template <int DK>
+// chunk-relative index * heads + head, workgroup u % nprep; NWS waves a unit.
+template <int DK, int NWS>
 __device__ __forceinline__ void prep_role(PrepSmem<DK> &sm, int wg, int nprep, const __hip_bfloat16 *__restrict__ q,
                                           const __hip_bfloat16 *__restrict__ k, const float *__restrict__ g,
                                           const float *__restrict__ beta, int L, int H, int heads, int nchunks,
@@ -1104,7 +1105,7 @@ __device__ __forceinline__ void prep_role(PrepSmem<DK> &sm, int wg, int nprep, c
     for (int u = wg; u < units; u += nprep) {
         const int c = pbeg + u / heads, bh = u % heads;
         __syncthreads();  // the previous unit's LDS reads are done
-        prep_unit<DK>(sm, q, k, g, beta, L, H, nchunks, ws, bh, c);
+        prep_unit<DK, NWS>(sm, q, k, g, beta, L, H, nchunks, ws, bh, c);
     }
 }
 
@@ -1122,20 +1123,22 @@ __global__ __launch_bounds__(256) void prefill_stage_kernel(
     __shared__ FusedLds<DK> sm;
     const int wg = blockIdx.x;
     if (wg < nprep)
-        prep_role<DK>(sm.prep, wg, nprep, q, k, g, beta, L, H, heads, nchunks, pbeg, pend, ws);
+        prep_role<DK, 4>(sm.prep, wg, nprep, q, k, g, beta, L, H, heads, nchunks, pbeg, pend, ws);
     else
         scan_role<DK, DV>(sm.scan, wg - nprep, nscan, S, q, k, v, L, H, nchunks, cbeg, cend, ws, o);
 }
 
 // Prep records of chunks [pbeg, pend) on the whole chip (two workgroups a
-// compute unit: this kernel needs only the prep's LDS).
+// compute unit: this kernel needs only the prep's LDS).  Nothing runs beside
+// it, so each unit takes 8 waves (the Gram tiles and the split spread over
+// twice the waves; the inverse keeps its 4): the unit's latency is the launch's.
 template <int DK>
-__global__ __launch_bounds__(256) void prefill_prep_kernel(
+__global__ __launch_bounds__(512) void prefill_prep_kernel(
     const __hip_bfloat16 *__restrict__ q, const __hip_bfloat16 *__restrict__ k, const float *__restrict__ g,
     const float *__restrict__ beta, int L, int H, int heads, int nchunks, int pbeg, int pend,
     uint8_t *__restrict__ ws) {
     __shared__ PrepSmem<DK> sm;
-    prep_role<DK>(sm, blockIdx.x, gridDim.x, q, k, g, beta, L, H, heads, nchunks, pbeg, pend, ws);
+    prep_role<DK, 8>(sm, blockIdx.x, gridDim.x, q, k, g, beta, L, H, heads, nchunks, pbeg, pend, ws);
 }
 
 template <int DK, int DV>
@@ -1172,7 +1175,7 @@ hipError_t launch_dk_dv(float *S, const void *q, const void *k, const void *v, c
         }
         bnd[nseg + 1] = nchunks;
         const int units0 = int(heads) * bnd[1];
-        hipLaunchKernelGGL((prefill_prep_kernel<DK>), dim3(unsigned(units0)), dim3(256), 0, st, qq, kk, g, beta, L,
+        hipLaunchKernelGGL((prefill_prep_kernel<DK>), dim3(unsigned(units0)), dim3(512), 0, st, qq, kk, g, beta, L,
                            s.H, int(heads), nchunks, 0, bnd[1], wsb);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
