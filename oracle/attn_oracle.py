@@ -26,6 +26,15 @@ Readings:
 import numpy as np
 
 
+def attn_row(q_row, keys, vals, scale):
+    """One query row: softmax over the visible keys of (keys . q_row * scale),
+    then the weighted sum of their values.  q_row [d], keys/vals [N][d] (the
+    visible positions, in order) -> [d]."""
+    s = np.asarray(keys, np.float64) @ np.asarray(q_row, np.float64) * scale
+    w = np.exp(s - s.max())
+    return (w / w.sum()) @ np.asarray(vals, np.float64)
+
+
 def attn_verify(q, k_new, v_new, k_cache, v_cache, ctx, scale):
     """q [B][T][Hq][d], k_new/v_new [B][T][Hkv][d], k_cache/v_cache
     [B][Lmax][Hkv][d], ctx [B] -> (o [B][T][Hq][d], k_cache', v_cache') with the
@@ -44,9 +53,7 @@ def attn_verify(q, k_new, v_new, k_cache, v_cache, ctx, scale):
                 g = h // group
                 keys = np.concatenate([kc[b, :c, g], kn[b, : t + 1, g]], axis=0)
                 vals = np.concatenate([vc[b, :c, g], vn[b, : t + 1, g]], axis=0)
-                s = keys @ q[b, t, h] * scale
-                w = np.exp(s - s.max())
-                o[b, t, h] = (w / w.sum()) @ vals
+                o[b, t, h] = attn_row(q[b, t, h], keys, vals, scale)
         kc[b, c: c + T] = kn[b]
         vc[b, c: c + T] = vn[b]
     return o, kc, vc

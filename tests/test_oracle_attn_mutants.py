@@ -9,7 +9,7 @@ from oracle import attn_oracle
 from tests import test_oracle_attn_pins as pins
 
 MUTANTS = [
-    ("scale dropped", "s = keys @ q[b, t, h] * scale", "s = keys @ q[b, t, h]"),
+    ("scale dropped", "np.asarray(q_row, np.float64) * scale", "np.asarray(q_row, np.float64)"),
     ("block row t not visible to itself", "kn[b, : t + 1, g]", "kn[b, :t, g]"),
     ("block rows after t visible", "vals = np.concatenate([vc[b, :c, g], vn[b, : t + 1, g]], axis=0)",
      "vals = np.concatenate([vc[b, :c, g], vn[b, :, g]], axis=0)"),
@@ -18,7 +18,8 @@ MUTANTS = [
     ("values read from the keys", "vals = np.concatenate([vc[b, :c, g], vn[b, : t + 1, g]], axis=0)",
      "vals = np.concatenate([kc[b, :c, g], kn[b, : t + 1, g]], axis=0)"),
     ("append one row late", "kc[b, c: c + T] = kn[b]", "kc[b, c + 1: c + 1 + T] = kn[b][: kc.shape[1] - c - 1]"),
-    ("softmax without normalising", "o[b, t, h] = (w / w.sum()) @ vals", "o[b, t, h] = w @ vals"),
+    ("softmax without normalising", "return (w / w.sum()) @ np.asarray(vals, np.float64)",
+     "return w @ np.asarray(vals, np.float64)"),
 ]
 
 PINS = [pins.test_hand_example, pins.test_equal_scores_average_the_values, pins.test_dominant_key_selects_its_value,
