@@ -80,14 +80,18 @@ def accept_greedy(target_logits, draft_tokens):
     return n, nxt
 
 
-def accept_sampled(target_logits, draft_logits, draft_tokens, u_accept, u_sample, tau):
+def accept_sampled(target_logits, draft_logits, draft_tokens, u_accept, u_sample, tau, flip=None):
     """Exact speculative sampling over one verify block per sequence.
 
     target_logits [B][T][V], draft_logits [B][T-1][V], draft_tokens [B][T-1],
     u_accept [B][T-1], u_sample [B]  ->  (n [B], next_token [B], info), where
     info[b] = dict(m=kept drafts, kind="correction"|"bonus", accept_margins=[...],
     draw_margin=...).  An accept margin is |u q(d) - p(d)| / max(p(d), q(d)): how
-    far that decision is from its threshold."""
+    far that decision is from its threshold.
+
+    flip: optional {b: set of draft indices}; those keep decisions of sequence b
+    go the other way.  A decision within rounding of its threshold can go either
+    way in a lower precision, and this gives the outcome on the other branch."""
     z = np.asarray(target_logits, dtype=np.float64)
     y = np.asarray(draft_logits, dtype=np.float64)
     d = np.asarray(draft_tokens)
@@ -106,7 +110,10 @@ def accept_sampled(target_logits, draft_logits, draft_tokens, u_accept, u_sample
             tok = int(d[b, m])
             lhs, rhs = ua[b, m] * q[tok], p[tok]
             margins.append(abs(lhs - rhs) / max(p[tok], q[tok], 1e-300))
-            if lhs < rhs:
+            keep = lhs < rhs
+            if flip is not None and m in flip.get(b, ()):
+                keep = not keep
+            if keep:
                 m += 1
             else:
                 break

@@ -15,8 +15,8 @@ SRC = accept_oracle.__file__
 
 # (name, original text, planted text); the original occurs exactly once.
 MUTANTS = [
-    ("keep test inverted to u p < q", "if lhs < rhs:", "if ua[b, m] * p[tok] < q[tok]:"),
-    ("keep test without the drafter's q", "if lhs < rhs:", "if ua[b, m] < rhs:"),
+    ("keep test inverted to u p < q", "keep = lhs < rhs", "keep = ua[b, m] * p[tok] < q[tok]"),
+    ("keep test without the drafter's q", "keep = lhs < rhs", "keep = ua[b, m] < rhs"),
     ("correction from q - p", 'w, kind = np.maximum(p - q, 0.0), "correction"',
      'w, kind = np.maximum(q - p, 0.0), "correction"'),
     ("correction drawn from p", 'w, kind = np.maximum(p - q, 0.0), "correction"', 'w, kind = p, "correction"'),

@@ -151,3 +151,33 @@ def test_greedy_is_the_cold_limit_of_sampled():
     # the bonus (p one-hot) always; a correction's residual max(0, p - q) is one-hot
     # at p's argmax too.
     assert np.array_equal(xg, xs)
+
+
+def test_flip_matches_forcing_the_branch_through_u():
+    """accept_sampled(..., flip) takes the named keep decisions the other way.  The
+    same branch can be forced through the inputs: u = 0 keeps any draft with
+    p(d) > 0, and u = 1e9 rejects any draft with q(d) > 0.  Both routes must give
+    the same n, token and later decisions."""
+    rng = np.random.default_rng(17)
+    B, T, V, tau = 24, 8, 40, 1.0
+    z = rng.normal(size=(B, T, V)) * 2
+    y = z[:, : T - 1] + rng.normal(size=(B, T - 1, V))
+    d = rng.integers(0, V, size=(B, T - 1))
+    ua, us = rng.random((B, T - 1)), rng.random(B)
+    _, _, info = A.accept_sampled(z, y, d, ua, us, tau)
+    tried = 0
+    for b in range(B):
+        for j in range(len(info[b]["accept_margins"])):
+            kept = j < info[b]["m"]
+            u2 = ua.copy()
+            u2[b, j] = 1e9 if kept else 0.0
+            rn, rx, ri = A.accept_sampled(z[b:b + 1], y[b:b + 1], d[b:b + 1], u2[b:b + 1], us[b:b + 1], tau)
+            fn, fx, fi = A.accept_sampled(z[b:b + 1], y[b:b + 1], d[b:b + 1], ua[b:b + 1], us[b:b + 1], tau,
+                                          flip={0: {j}})
+            assert (rn[0], rx[0], ri[0]["m"], ri[0]["kind"]) == (fn[0], fx[0], fi[0]["m"], fi[0]["kind"])
+            if kept:
+                assert fn[0] == j + 1 and fi[0]["kind"] == "correction"
+            else:
+                assert fn[0] >= j + 2
+            tried += 1
+    assert tried >= B
