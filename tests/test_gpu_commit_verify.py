@@ -87,6 +87,32 @@ def test_fused_chain_matches_oracle(G, dk, dv):
     assert torch.equal(pos, sum(ns))
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+@pytest.mark.parametrize("T", [1, 3, 8, 12, 16])
+@pytest.mark.parametrize("B,H", [(2, 4), (8, 32)], ids=["few_heads", "head_per_wg"])
+def test_fused_chain_block_lengths(G, B, H, T, dtype):
+    """Chains of fused passes at every block length class (T <= 8 and the
+    two-tile form for T = 9 .. 16), fp32 and bf16 block inputs, in both launch
+    shapes: fewer than 256 (instance, head) pairs (32 value rows per
+    workgroup) and 256 pairs (a head per workgroup)."""
+    d, R = 128, 4
+    seed = 60 + T + (0 if dtype == torch.bfloat16 else 100) + B
+    print_case(test="fused_chain_T", B=B, H=H, d=d, T=T, dtype=dtype, rounds=R, seed=seed)
+    x = make_inputs(B, H, d, d, T * R, dtype=dtype, seed=seed, device=DEV)
+    blocks = blocks_of(x, T, R)
+    gen = torch.Generator().manual_seed(seed)
+    ns = [torch.randint(0, T + 1, (B,), generator=gen, dtype=torch.int32).to(DEV) for _ in range(R)]
+    ns[1][0] = T
+    ns[2][-1] = 0
+    S = x.S0.clone()
+    outs, pos, _ = run_chain(G, S, blocks, ns, T)
+    ref_outs, ref_S = oracle_chain(x.S0, blocks, ns)
+    for r in range(R):
+        assert rel_err_outputs(outs[r], ref_outs[r]) <= OUT_TOL, r
+    assert rel_err_state(S, ref_S) <= STATE_TOL
+    assert torch.equal(pos, sum(ns))
+
+
 def test_fused_equals_separate_calls(G):
     B, H, d, T, R = 4, 8, 128, 8, 5
     print_case(test="fused_vs_separate", B=B, H=H, d=d, T=T, rounds=R, seed=53)
