@@ -2,19 +2,22 @@
 """Benchmark of the GDN speculative-verify hot path on one MI355X.
 
 A step is one speculative pass over a 48-GDN-layer model (32 heads per layer,
-dk = dv = 128, bf16 q/k/v, fp32 state): gdn_verify_block on a T = 8 block for
-all 48 layers in one launch, then gdn_commit at the pass's accepted length
-n ~ Uniform{0..8} (the same n for all layers of a pass), read on the device.
-The headline value is committed tokens per second.
+dk = dv = 128, bf16 q/k/v, fp32 state): one gdn_commit_verify launch over all
+48 layers commits the block pending from the previous pass at that pass's
+accepted length n ~ Uniform{0..8} (the same n for all layers, read on the
+device) and verifies the next T = 8 block.  The headline value is committed
+tokens per second; the accepted lengths come in pairs (n, 8 - n), so every
+timed window commits exactly 4 tokens a pass on average.
 
-The chunked prefill (one layer, 32 heads, 4,096-token prompt, chunk 64) is
+The same passes as separate gdn_verify_block + gdn_commit calls, each kernel
+alone, the chunked prefill (one layer, 32 heads, 4,096-token prompt, chunk 64;
+and 48 layers x 32,768 tokens followed by 256 rounds on the prefilled state),
+plain decode, acceptance, the full-attention layers and the GDN mixer are
 timed in the same run and reported beside it.
 
 Inputs are synthetic (speculative_verify_amd.inputs) and already resident in
-HBM.  Four independent buffer sets rotate across passes and each commit lags
-its verify by two passes, so no kernel finds its state still in the 256 MB
-Infinity Cache from the previous kernel; every step still does exactly one
-48-layer verify and one 48-layer commit.
+HBM.  Four independent buffer sets rotate across passes, so no kernel finds
+its state still in the 256 MB Infinity Cache from the previous kernel.
 """
 from __future__ import annotations
 
@@ -164,11 +167,16 @@ def load_traffic(kernel):
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
-def accept_count(args):
-    """Passes whose accepted lengths are drawn: warmup, the fused headline and
-    kernel-timing regions, and the two regions of separate calls (each with LAG
-    passes verified ahead)."""
-    return args.warmup + 4 * args.steps + 2 * LAG
+def accept_plan(args):
+    """The accepted lengths of every region, in launch order: warmup and headline
+    passes of the fused kernel, the separate calls' commits, the commit-alone
+    region's commits.  Each region draws its own paired sequence (n, 8 - n)."""
+    from speculative_verify_amd.inputs import make_accepts_paired
+
+    return {"warm": [int(v) for v in make_accepts_paired(args.warmup, T, seed=args.seed)],
+            "head": [int(v) for v in make_accepts_paired(args.steps, T, seed=args.seed + 1)],
+            "sep": [int(v) for v in make_accepts_paired(args.steps, T, seed=args.seed + 2)],
+            "com": [int(v) for v in make_accepts_paired(args.steps, T, seed=args.seed + 3)]}
 
 
 class KernelEvents:
@@ -229,11 +237,11 @@ def cpu_baseline(args):
     import torch
 
     import oracle
-    from speculative_verify_amd.inputs import make_accepts, make_inputs
+    from speculative_verify_amd.inputs import make_accepts_paired, make_inputs
 
     x = make_inputs(LAYERS, HEADS, DK, DV, T, seed=args.seed + 1000)
     f64 = [t.double().numpy() for t in (x.S0, x.q, x.k, x.v, x.g, x.beta)]
-    ns = make_accepts(64, T, seed=args.seed + 1000).numpy()
+    ns = make_accepts_paired(64, T, seed=args.seed + 1000).numpy()
     passes, tokens = 0, 0
     t0 = time.perf_counter()
     while True:
@@ -263,7 +271,7 @@ def main():
     import torch
 
     import speculative_verify_amd.gdn as G
-    from speculative_verify_amd.inputs import make_accepts, make_inputs
+    from speculative_verify_amd.inputs import make_inputs
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -280,105 +288,122 @@ def main():
         o = torch.empty(LAYERS, T, HEADS, DV, dtype=torch.float32, device=dev)
         recs = [G.new_record(x.S0, T, dt) for _ in range(3)]
         sets.append((x, o, recs))
-    total = accept_count(args)
-    n_host = make_accepts(total, T, seed=args.seed)
-    n_dev = n_host.view(total, 1).expand(total, LAYERS).contiguous().to(dev)
+    # Accepted lengths: every region draws its own paired sequence (n, 8 - n), so
+    # each timed window commits exactly 4 tokens per pass on average.
+    plan = accept_plan(args)
+    n_head, n_sep, n_com = plan["head"], plan["sep"], plan["com"]
+    per_layer = lambda n: torch.tensor(n, dtype=torch.int32).view(-1, 1).expand(-1, LAYERS).contiguous().to(dev)
+    n_head_d, n_sep_d, n_com_d = per_layer(n_head), per_layer(n_sep), per_layer(n_com)
     pos = torch.zeros(LAYERS, dtype=torch.int32, device=dev)
 
     # Fused path (the headline): step s runs on set s % RING one
-    # gdn_commit_verify -- commit the block pending there at n_host[s], then verify
+    # gdn_commit_verify -- commit the block pending there at n[s], then verify
     # the set's next block -- alternating the set's first two records.
-    def fused(s, kev=None, evs=None):
+    def fused(s, n):
         x, o, recs = sets[s % RING]
         visit = s // RING
-        if evs is not None:
-            kev.record(evs[0])
-        G.gdn_commit_verify(x.S0, recs[visit % 2], n_dev[s], x.q, x.k, x.v, x.g, x.beta, o,
-                            recs[(visit + 1) % 2], pos=pos)
-        if evs is not None:
-            kev.record(evs[1])
+        G.gdn_commit_verify(x.S0, recs[visit % 2], n, x.q, x.k, x.v, x.g, x.beta, o, recs[(visit + 1) % 2],
+                            pos=pos)
 
     for r in range(RING):  # a pending block on every set
         x, o, recs = sets[r]
         G.gdn_verify_block(x.S0, x.q, x.k, x.v, x.g, x.beta, o, recs[0])
+    warm_n = per_layer(plan["warm"]) if args.warmup else None
     for s in range(args.warmup):
-        fused(s)
+        fused(s, warm_n[s])
     torch.cuda.synchronize()
 
     # Headline region: exactly `steps` passes back to back, nothing between the
-    # launches, wall clock around device synchronisations.
+    # launches.  The wall clock runs between device synchronisations; two events
+    # on the launch stream bracket the same launches, so their interval over
+    # `steps` is the kernel's average duration per launch (back-to-back launches,
+    # no per-launch events), never above the wall time per step.
+    kev = KernelEvents(torch, torch.cuda.current_stream())
+    ev_a, ev_b = kev.new(), kev.new()
     t0 = time.perf_counter()
+    kev.record(ev_a)
     for i in range(args.steps):
-        fused(args.warmup + i)
+        fused(args.warmup + i, n_head_d[i])
+    kev.record(ev_b)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    n_timed = [int(v) for v in n_host[args.warmup:args.warmup + args.steps]]
+    avg_fus_ms = kev.ms(ev_a, ev_b) / args.steps
+    n_timed = [int(v) for v in n_head]
     tokens = sum(n_timed)
-
-    # Kernel-timing region: the next `steps` passes with events on the launch
-    # stream around each kernel (the events add a little time of their own, so
-    # these per-launch averages are upper bounds on the kernels' durations).
-    kev = KernelEvents(torch, torch.cuda.current_stream())
     s1 = args.warmup + args.steps
-    evs = [[kev.new() for _ in range(2)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        fused(s1 + i, kev, evs[i])
-    torch.cuda.synchronize()
-    t_fus = [kev.ms(e[0], e[1]) for e in evs]
-    kev.free([e for ev in evs for e in ev])
-    n_fk = [int(v) for v in n_host[s1:s1 + args.steps]]
 
     # Separate calls: the same passes as gdn_verify_block + gdn_commit.  Pass p is
     # verified on set p % RING and committed LAG steps later (so that a commit
     # never finds the state its verify just read in the cache); the set's third
     # record carries the block.
-    s2 = s1 + args.steps
-
     def verify(p):
         x, o, recs = sets[p % RING]
         G.gdn_verify_block(x.S0, x.q, x.k, x.v, x.g, x.beta, o, recs[2])
 
-    def commit(p):
+    def commit(p, n):
         x, _, recs = sets[p % RING]
-        G.gdn_commit(x.S0, recs[2], n_dev[p], pos)
+        G.gdn_commit(x.S0, recs[2], n, pos)
 
-    def separate(s, evs=None):
-        if evs is not None:
-            kev.record(evs[0])
-        verify(s + LAG)
-        if evs is not None:
-            kev.record(evs[1])
-        commit(s)
-        if evs is not None:
-            kev.record(evs[2])
-
+    s2 = s1
     for p in range(s2, s2 + LAG):
         verify(p)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        separate(s2 + i)
+        verify(s2 + i + LAG)
+        commit(s2 + i, n_sep_d[i])
     torch.cuda.synchronize()
     wall_sep = time.perf_counter() - t0
-    tokens_sep = sum(int(v) for v in n_host[s2:s2 + args.steps])
-    s3 = s2 + args.steps
-    for p in range(s3, s3 + LAG):  # re-prime (the headline region above consumed them)
-        verify(p)
-    evs = [[kev.new() for _ in range(3)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        separate(s3 + i, evs[i])
+    tokens_sep = sum(int(v) for v in n_sep)
+    for p in range(s2 + args.steps, s2 + args.steps + LAG):  # the pending blocks left: committed, untimed
+        commit(p, n_sep_d[0])
     torch.cuda.synchronize()
-    t_ver = [kev.ms(e[0], e[1]) for e in evs]
-    t_com = [kev.ms(e[1], e[2]) for e in evs]
-    kev.free([e for ev in evs for e in ev])
-    n_kt = [int(v) for v in n_host[s3:s3 + args.steps]]
 
-    avg_fus_ms = sum(t_fus) / len(t_fus)
-    avg_ver_ms = sum(t_ver) / len(t_ver)
-    avg_com_ms = sum(t_com) / len(t_com)
+    # Verify alone: `steps` launches back to back over the rotating sets (verify
+    # never writes the state), bracketed by two events.
+    kev.record(ev_a)
+    for i in range(args.steps):
+        verify(i)
+    kev.record(ev_b)
+    torch.cuda.synchronize()
+    avg_ver_ms = kev.ms(ev_a, ev_b) / args.steps
+
+    # Commit alone: a pool of states, each with a pending block verified (untimed)
+    # and the caches flushed, then the pool's commits back to back between two
+    # events; repeated until `steps` commits are timed.  The flush reads a 512 MiB
+    # buffer: it evicts the states (writing back whatever the verifies left dirty,
+    # untimed) and leaves only clean lines, so the timed commits write back
+    # nothing of the flush's.
+    POOL = min(args.steps, 8)
+    pool = []
+    for _ in range(POOL):
+        S_p = torch.empty_like(sets[0][0].S0)
+        pool.append((S_p, G.new_record(S_p, T, dt)))
+    flush = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
+    com_ms, done = 0.0, 0
+    while done < args.steps:
+        cnt = min(POOL, args.steps - done)
+        for j in range(cnt):
+            x, o, _ = sets[j % RING]
+            pool[j][0].copy_(x.S0)
+            G.gdn_verify_block(pool[j][0], x.q, x.k, x.v, x.g, x.beta, o, pool[j][1])
+        flush.sum(dtype=torch.int64)
+        torch.cuda.synchronize()
+        kev.record(ev_a)
+        for j in range(cnt):
+            G.gdn_commit(pool[j][0], pool[j][1], n_com_d[done + j], pos)
+        kev.record(ev_b)
+        torch.cuda.synchronize()
+        com_ms += kev.ms(ev_a, ev_b)
+        done += cnt
+    avg_com_ms = com_ms / args.steps
+    kev.free([ev_a, ev_b])
+    del pool, flush
+    torch.cuda.empty_cache()
+
     vb = verify_bytes(LAYERS, HEADS, DK, DV, T, es)
-    fb_avg = sum(fused_bytes(LAYERS, HEADS, DK, DV, T, n, es) for n in n_fk) / len(n_fk)
-    cb_avg = sum(commit_bytes(LAYERS, HEADS, DK, DV, n, es) for n in n_kt) / len(n_kt)
+    fb_avg = sum(fused_bytes(LAYERS, HEADS, DK, DV, T, n, es) for n in n_timed) / len(n_timed)
+    cb_avg = sum(commit_bytes(LAYERS, HEADS, DK, DV, int(n), es) for n in n_com) / len(n_com)
     fus_gbs = fb_avg / (avg_fus_ms * 1e-3) / 1e9
     ver_gbs = vb / (avg_ver_ms * 1e-3) / 1e9
     com_gbs = cb_avg / (avg_com_ms * 1e-3) / 1e9
@@ -415,13 +440,18 @@ def main():
                    "path": "gdn_commit_verify (commit of the pending block and verify of the next "
                            "in one pass over the state)",
                    "layers": LAYERS, "heads": HEADS, "dk": DK, "dv": DV, "T": T,
-                   "input_dtype": "bf16", "tokens_committed": tokens},
+                   "input_dtype": "bf16", "tokens_committed": tokens,
+                   "accepted_lengths": "pairs (n, 8 - n), n ~ U{0..8}: every even window averages 4"},
         "rows_per_s": round(T * args.steps / wall, 1),
         "pass_hbm_frac": round(fus_gbs / HBM_PEAK_GBS, 4),
         "separate_calls": {"tokens_per_s": round(tokens_sep / wall_sep, 1),
                            "ms_per_step": round(wall_sep / args.steps * 1e3, 4),
                            "path": "gdn_verify_block + gdn_commit"},
-        "kernel_timing": {"events": kev.kind, "region": f"{args.steps} passes after the headline region"},
+        "kernel_timing": {"events": kev.kind,
+                          "region": f"two events bracketing {args.steps} back-to-back launches on the launch "
+                                    f"stream: gdn_commit_verify over the headline region itself, gdn_verify_block "
+                                    f"over its own region, gdn_commit over batches of {POOL} pending states "
+                                    f"(each batch after a cache flush); average = interval / launches"},
         "sources_sha256_16": sources_hash(),
         "roofline": roof,
         "kernels": kernels,
@@ -432,7 +462,8 @@ def main():
     if not args.no_prefill:
         result["prefill"] = bench_prefill(args, G, dev)
     if not args.no_prefill_long:
-        result["prefill_long"] = bench_prefill(args, G, dev, B=PFL_B, L=PFL_L, reps=3, flush_mib=0, traffic_key=None)
+        result["prefill_long"] = bench_prefill(args, G, dev, B=PFL_B, L=PFL_L, reps=3, flush_mib=0, traffic_key=None,
+                                               rounds=256)
     if not args.no_decode:
         result["decode"] = bench_decode(args, G, dev)
     if not args.no_accept:
@@ -515,6 +546,12 @@ def _read_csv(pattern):
         return list(csv.DictReader(f))
 
 
+def _cmd_arg(cmd, flag, default):
+    """The integer value of `flag` in a command line, else `default`."""
+    parts = cmd.split()
+    return int(parts[parts.index(flag) + 1]) if flag in parts else default
+
+
 def summarize_profiles(args):
     """Write the profile summaries from one directory of rocprofv3 output:
       stats/**/*kernel_stats.csv            --kernel-trace --stats run of bench.py
@@ -525,8 +562,6 @@ def summarize_profiles(args):
     raw counters (per dispatch, KiB) to bytes.  --steps/--warmup/--seed must be
     those of the counter runs: the commit's accepted lengths, and so its
     algorithmic bytes, follow from them."""
-    from speculative_verify_amd.inputs import make_accepts
-
     d = args.summarize
     with open(os.path.join(d, "commands.txt")) as f:
         commands = [ln.rstrip("\n") for ln in f if ln.strip()]
@@ -547,6 +582,20 @@ def summarize_profiles(args):
         lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                      f"{float(r['TotalDurationNs']) / total:.3f} |")
+    # The headline region alone: the fused 48-layer kernel's launches after the
+    # warmup, by launch order in the kernel trace (the long prompt's rounds run the
+    # same kernel later in the run).
+    trace = _read_csv(os.path.join(d, "stats", "**", "*kernel_trace.csv"))
+    fus = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in trace
+                 if "verify_kernel" in r["Kernel_Name"] and ", true, 4, false>" in r["Kernel_Name"])
+    steps, warm = _cmd_arg(commands[0], "--steps", 500), _cmd_arg(commands[0], "--warmup", 20)
+    head = fus[warm:warm + steps]
+    if head:
+        avg = sum(e - b for b, e in head) / len(head) / 1e3
+        span = (head[-1][1] - head[0][0]) / len(head) / 1e3
+        lines += ["", f"Headline region (`gdn_commit_verify`, 48 layers x 32 heads, T=8, launches {warm} .. "
+                      f"{warm + steps - 1} of that kernel): average kernel duration {avg:.2f} us over {len(head)} "
+                      f"launches; first start to last end {span:.2f} us per launch."]
     with open(STATS_MD, "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -592,8 +641,7 @@ def summarize_profiles(args):
                "calibration": {"copy_kib": calib_kib, "dispatches": len(cal),
                                "fetch_factor": round(fetch_factor, 4), "write_factor": round(write_factor, 4)},
                "kernels": {}}
-    total = accept_count(args)
-    n_host = [int(v) for v in make_accepts(total, T, seed=args.seed)]
+    plan = accept_plan(args)
 
     def summarize(rows, alg):
         fr = sum(r[1] for r in rows) / len(rows)
@@ -603,15 +651,17 @@ def summarize_profiles(args):
                 "hbm_bytes_per_launch": round(fr + wr), "algorithmic_bytes_per_launch": round(ab),
                 "traffic_over_algorithmic": round((fr + wr) / ab, 3)}
 
-    # The fused kernel's dispatch i runs pass i (warmup, headline, kernel-timing
-    # regions); the separate commits run passes warmup + 2 steps + i.
-    # (Four tiles a wave: the 48-layer launches; the plain-decode leg's few-heads
-    # launches are not in the counter runs.)
+    # The fused kernel's dispatches run the warmup passes, then the headline
+    # passes; the separate calls' commits come first among the commit kernel's
+    # dispatches, then the commit-alone region's.  (Four tiles a wave: the
+    # 48-layer launches; the plain-decode leg's few-heads launches and the
+    # long-prompt rounds are not in the counter runs.)
+    fus_n = plan["warm"] + plan["head"]
     fus = kernel_rows("verify_kernel", ", true, 4, false>")
     if fus:
-        fus = fus[:total]
+        fus = fus[:len(fus_n)]
         summary["kernels"]["commit_verify_kernel"] = summarize(
-            fus, [fused_bytes(LAYERS, HEADS, DK, DV, T, n_host[i], es) for i in range(len(fus))])
+            fus, [fused_bytes(LAYERS, HEADS, DK, DV, T, fus_n[i], es) for i in range(len(fus))])
     ver = kernel_rows("verify_kernel", ", false, 4, false>")
     if ver:
         vb = verify_bytes(LAYERS, HEADS, DK, DV, T, es)
@@ -621,12 +671,12 @@ def summarize_profiles(args):
             "dispatches": len(ver), "read_bytes": round(fr), "write_bytes": round(wr),
             "hbm_bytes_per_launch": round(fr + wr), "algorithmic_bytes_per_launch": vb,
             "traffic_over_algorithmic": round((fr + wr) / vb, 3)}
+    com_n = plan["sep"] + [plan["sep"][0]] * LAG + plan["com"]
     com = kernel_rows("commit_kernel")
     if com:
-        s2 = args.warmup + 2 * args.steps
-        com = com[:total - s2]
+        com = com[:len(com_n)]
         summary["kernels"]["commit_kernel"] = summarize(
-            com, [commit_bytes(LAYERS, HEADS, DK, DV, n_host[s2 + i], es) for i in range(len(com))])
+            com, [commit_bytes(LAYERS, HEADS, DK, DV, com_n[i], es) for i in range(len(com))])
     # Prefill: every call launches either prefill_kernel, or one prep launch and
     # one stage launch per chunk segment; per call.
     pk = kernel_rows("prefill_kernel<")
@@ -849,12 +899,12 @@ def bench_mixer(args, G, dev):
     the last-level cache."""
     import torch
 
-    from speculative_verify_amd.inputs import make_accepts, make_inputs, make_mixer_inputs
+    from speculative_verify_amd.inputs import make_accepts_paired, make_inputs, make_mixer_inputs
 
     L, H, NSET = LAYERS, HEADS, 4
     x = make_inputs(L, H, DK, DV, T, seed=args.seed + 61, device=dev, device_gen=True)
     m = make_mixer_inputs(L, T, H, MIX_HK, DK, seed=args.seed + 61, device=dev)
-    ns = make_accepts(64, T, seed=args.seed + 61)
+    ns = make_accepts_paired(64, T, seed=args.seed + 61)
     nt = [torch.full((L,), int(v), dtype=torch.int32, device=dev) for v in ns]
     y = torch.empty(L, T, H, DV, dtype=torch.float32, device=dev)
     Ss = [x.S0.clone() for _ in range(NSET)]
@@ -936,9 +986,50 @@ def bench_attn(args, G, dev):
     return out
 
 
-def bench_prefill(args, G, dev, B=PF_B, L=PF_L, reps=None, flush_mib=512, traffic_key="prefill"):
+def bench_rounds(G, dev, S, rounds, seed):
+    """Speculative rounds on a prefilled state: `rounds` gdn_commit_verify launches
+    back to back on the one state S [B][H][dv][dk] (the model's own: no rotation,
+    so the 256 MB last-level cache may hold part of it), each committing the
+    previous round's block at its accepted length and verifying the next T = 8
+    block; paired accepted lengths, so the rounds commit exactly 4 tokens each on
+    average.  Timed with two events around the launches."""
+    import torch
+
+    from speculative_verify_amd.inputs import make_accepts_paired, make_inputs
+
+    B, H = S.shape[0], S.shape[1]
+    blocks = [make_inputs(B, H, DK, DV, T, seed=seed + i, device=dev, device_gen=True) for i in range(8)]
+    recs = [G.new_record(S, T, torch.bfloat16) for _ in range(2)]
+    ns = make_accepts_paired(rounds, T, seed=seed)
+    nd = ns.view(-1, 1).expand(-1, B).contiguous().to(dev)
+    o = torch.empty(B, T, H, DV, dtype=torch.float32, device=dev)
+    pos = torch.zeros(B, dtype=torch.int32, device=dev)
+    x0 = blocks[0]
+    G.gdn_verify_block(S, x0.q, x0.k, x0.v, x0.g, x0.beta, o, recs[0])
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for r in range(rounds):
+        x = blocks[(r + 1) % len(blocks)]
+        G.gdn_commit_verify(S, recs[r % 2], nd[r], x.q, x.k, x.v, x.g, x.beta, o, recs[(r + 1) % 2], pos=pos)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) / rounds * 1e3
+    tokens = int(ns.sum())
+    nbytes = sum(fused_bytes(B, H, DK, DV, T, int(v), 2) for v in ns) / rounds
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"workload": f"{rounds} speculative rounds (gdn_commit_verify, T={T}, n~U{{0..8}} in pairs) on the "
+                        f"state of the {B}-layer prefill, one state, back to back",
+            "rounds": rounds, "tokens_committed": tokens, "us_per_round": round(us, 2),
+            "tokens_per_s": round(tokens / (us * 1e-6 * rounds), 1),
+            "hbm": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_launch": round(nbytes)}}
+
+
+def bench_prefill(args, G, dev, B=PF_B, L=PF_L, reps=None, flush_mib=512, traffic_key="prefill", rounds=0):
     """Chunked prefill of B layers x PF_H heads over an L-token prompt, timed with
-    events over `reps` calls; a token counts once it has passed all B layers."""
+    events over `reps` calls; a token counts once it has passed all B layers.
+    With `rounds`, that many speculative rounds then run on the prefilled state."""
     import torch
 
     from speculative_verify_amd.inputs import make_inputs
@@ -967,7 +1058,10 @@ def bench_prefill(args, G, dev, B=PF_B, L=PF_L, reps=None, flush_mib=512, traffi
         b.record()
         torch.cuda.synchronize()
         t_ms.append(a.elapsed_time(b))
-    del x, o, S, ws, flush
+    del x, o, ws, flush
+    torch.cuda.empty_cache()
+    rounds_out = bench_rounds(G, dev, S, rounds, args.seed + 333) if rounds else None
+    del S
     torch.cuda.empty_cache()
     avg = sum(t_ms) / len(t_ms)
     fl = prefill_flops(B, PF_H, DK, DV, L, PF_C)
@@ -985,7 +1079,8 @@ def bench_prefill(args, G, dev, B=PF_B, L=PF_L, reps=None, flush_mib=512, traffi
             "hbm": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_launch": by,
                     "traffic": load_traffic(traffic_key) if traffic_key else None},
-            "mfma_counters": load_mfma("prefill" if B == PF_B and L == PF_L else "prefill_long")}
+            "mfma_counters": load_mfma("prefill" if B == PF_B and L == PF_L else "prefill_long"),
+            **({"rounds_after": rounds_out} if rounds_out else {})}
 
 
 if __name__ == "__main__":

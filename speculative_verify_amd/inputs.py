@@ -78,6 +78,18 @@ def make_accepts(count: int, T: int, *, seed: int = 0) -> torch.Tensor:
     return torch.randint(0, T + 1, (count,), generator=gen, dtype=torch.int32)
 
 
+def make_accepts_paired(count: int, T: int, *, seed: int = 0) -> torch.Tensor:
+    """Accepted-row counts in pairs (n, T - n) with n ~ Uniform{0..T}: each entry is
+    still Uniform{0..T}, and every window that starts at an even index and has an
+    even length averages exactly T / 2, so a timed window's token count does not
+    depend on the luck of the draw.  An odd count ends with T // 2."""
+    half = make_accepts((count + 1) // 2, T, seed=seed)
+    out = torch.stack([half, T - half], dim=1).flatten()[:count].clone()
+    if count % 2:
+        out[-1] = T // 2
+    return out.to(torch.int32)
+
+
 # ---------------------------------------------------------------------------
 # Acceptance inputs: logits of one verify block per sequence, standing in for a
 # target model and its drafter (no weights or vocabulary file involved).
