@@ -301,6 +301,33 @@ int gdn_accept_sampled(const void *target_logits, const void *draft_logits, gdn_
                        void *ws, size_t ws_bytes, void *hip_stream);
 
 /*
+ * gdn_accept_sampled without a workspace argument, for callers that cannot
+ * allocate device memory at call time (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the workspace is the
+ * library's own scratch, a file-scope device array of
+ * gdn_accept_noalloc_max_bytes() bytes (1 MiB) on each device the call runs on,
+ * held until the process ends.  Same arguments, results and errors as
+ * gdn_accept_sampled, except:
+ *   - no ws / ws_bytes; a shape whose workspace
+ *     (gdn_accept_workspace_bytes(shp, 1)) exceeds the scratch returns GDN_EWS
+ *     before anything is launched (about 100 sequences at T = 8, V = 151,936);
+ *   - the call runs on the stream's device (the current device for the null
+ *     stream); the first call on a device resolves that device's scratch once
+ *     (hipGetSymbolAddress), and no call allocates or frees memory;
+ *   - every call on a device shares that device's scratch: calls that overlap
+ *     on one device (on different streams, or from different threads) race and
+ *     must be ordered by the caller.  Nothing in the scratch needs clearing
+ *     between calls.
+ */
+int gdn_accept_sampled_noalloc(const void *target_logits, const void *draft_logits, gdn_in_dtype dt,
+                               const int32_t *draft_tokens, const float *u_accept, const float *u_sample,
+                               float temperature, const gdn_accept_shape *shp, int32_t *n_out,
+                               int32_t *next_token, void *hip_stream);
+
+/* Bytes of the per-device scratch that gdn_accept_sampled_noalloc uses. */
+size_t gdn_accept_noalloc_max_bytes(void);
+
+/*
  * Rewind of the filter history (the short causal filter before the mixer keeps
  * its last W inputs).  In place: history[b] becomes the last W rows of
  * [history[b]; rows[b][0 .. n[b]-1]], the history as if only the n[b] confirmed

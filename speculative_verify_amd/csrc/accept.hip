@@ -27,6 +27,8 @@
 //          weight passes u times the total.
 #include <climits>
 
+#include <mutex>
+
 #include "gdn_internal.h"
 
 namespace gdn {
@@ -521,6 +523,56 @@ hipError_t launch_accept_sampled(const void *tgt, const void *drf, gdn_in_dtype 
                                 drafts, u_acc, u_samp, inv_tau, B, T, V, n_out, next, w, st);
     return accept_sampled_t(static_cast<const float *>(tgt), static_cast<const float *>(drf), drafts, u_acc, u_samp,
                             inv_tau, B, T, V, n_out, next, w, st);
+}
+
+// Scratch of gdn_accept_sampled_noalloc: the workspace of one sampled call (per
+// slice statistics, draw descriptors, slice masses), in device memory that the
+// library owns for the life of the process, so that the call allocates nothing.
+// Each device holds its own copy.  In host code `scratch` names a host-side
+// stand-in, never the device array: its device address comes from
+// hipGetSymbolAddress, resolved once per device (with that device current) and
+// kept in scratch_ptr[].  Every call on a device shares that device's array;
+// calls that overlap on one device race.
+namespace {
+static __device__ __align__(256) uint8_t scratch[kAcceptScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::once_flag scratch_once[kMaxDevices];
+void *scratch_ptr[kMaxDevices];
+hipError_t scratch_err[kMaxDevices];
+
+// The device address of `scratch` on device `dev`, resolved on first use with
+// `dev` current (the caller's current device is restored).
+hipError_t scratch_on(int dev, void **out) {
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::call_once(scratch_once[dev], [dev] {
+        int cur = -1;
+        hipError_t e = hipGetDevice(&cur);
+        if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+        void *p = nullptr;
+        if (e == hipSuccess) e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur >= 0 && cur != dev) {
+            const hipError_t r = hipSetDevice(cur);
+            if (e == hipSuccess) e = r;
+        }
+        scratch_ptr[dev] = e == hipSuccess ? p : nullptr;
+        scratch_err[dev] = e == hipSuccess && p == nullptr ? hipErrorInvalidSymbol : e;
+    });
+    *out = scratch_ptr[dev];
+    return scratch_err[dev];
+}
+}  // namespace
+
+hipError_t launch_accept_sampled_noalloc(const void *tgt, const void *drf, gdn_in_dtype dt, const int32_t *drafts,
+                                         const float *u_acc, const float *u_samp, float inv_tau, int B, int T, int V,
+                                         int32_t *n_out, int32_t *next, hipStream_t st) {
+    if (accept_workspace_bytes(B, T, V, true) > kAcceptScratchBytes) return hipErrorInvalidValue;
+    int dev = -1;
+    hipError_t e = st != nullptr ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    void *ws = nullptr;
+    if ((e = scratch_on(dev, &ws)) != hipSuccess) return e;
+    return launch_accept_sampled(tgt, drf, dt, drafts, u_acc, u_samp, inv_tau, B, T, V, n_out, next, ws, st);
 }
 
 hipError_t launch_history_rewind(void *hist, const void *rows, const int32_t *n, int B, int W, int T, int C,

@@ -197,6 +197,27 @@ int gdn_accept_sampled(const void *target_logits, const void *draft_logits, gdn_
                                             static_cast<hipStream_t>(hip_stream)));
 }
 
+int gdn_accept_sampled_noalloc(const void *target_logits, const void *draft_logits, gdn_in_dtype dt,
+                               const int32_t *draft_tokens, const float *u_accept, const float *u_sample,
+                               float temperature, const gdn_accept_shape *shp, int32_t *n_out,
+                               int32_t *next_token, void *hip_stream) {
+    int rc = check_accept_shape(shp);
+    if (rc != GDN_OK) return rc;
+    if (!valid_dtype(dt)) return GDN_EINVAL;
+    if (!(temperature > 0.f) || !std::isfinite(temperature)) return GDN_ERANGE;
+    const size_t es = size_t(esize_of(dt));
+    if (!aligned(target_logits, es) || !aligned(u_sample, 4) || !aligned(n_out, 4) || !aligned(next_token, 4))
+        return GDN_EINVAL;
+    if (shp->T > 1 && (!aligned(draft_logits, es) || !aligned(draft_tokens, 4) || !aligned(u_accept, 4)))
+        return GDN_EINVAL;
+    if (accept_workspace_bytes(shp->B, shp->T, shp->V, true) > kAcceptScratchBytes) return GDN_EWS;
+    return hip_status(launch_accept_sampled_noalloc(target_logits, draft_logits, dt, draft_tokens, u_accept,
+                                                    u_sample, 1.f / temperature, shp->B, shp->T, shp->V, n_out,
+                                                    next_token, static_cast<hipStream_t>(hip_stream)));
+}
+
+size_t gdn_accept_noalloc_max_bytes(void) { return kAcceptScratchBytes; }
+
 int gdn_history_rewind(void *history, const void *rows, const int32_t *n, int32_t B, int32_t W, int32_t T,
                        int32_t C, gdn_in_dtype dt, void *hip_stream) {
     if (!valid_dtype(dt)) return GDN_EINVAL;

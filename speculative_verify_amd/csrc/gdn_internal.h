@@ -229,6 +229,11 @@ hipError_t launch_prefill(float *S, const void *q, const void *k, const void *v,
 // length (0 when the one-pass schedule is the faster one).
 size_t prefill_workspace_bytes(const gdn_shape &shp, int L);
 size_t accept_workspace_bytes(int B, int T, int V, bool sampled);
+// Size of the library's own scratch for gdn_accept_sampled_noalloc (per device).
+constexpr size_t kAcceptScratchBytes = size_t(1) << 20;
+hipError_t launch_accept_sampled_noalloc(const void *tgt, const void *drf, gdn_in_dtype dt, const int32_t *drafts,
+                                         const float *u_acc, const float *u_samp, float inv_tau, int B, int T, int V,
+                                         int32_t *n_out, int32_t *next, hipStream_t st);
 size_t attn_workspace_bytes(const gdn_attn_shape &s, int T);
 hipError_t launch_mixer_verify(const float *S, const gdn_mixer_inputs &in, int T, const gdn_shape &shp, float *y,
                                void *record, hipStream_t stream);

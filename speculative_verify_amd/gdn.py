@@ -33,6 +33,8 @@ EXPORTED = (
     "gdn_prefill_workspace_bytes",
     "gdn_prefill_chunked",
     "gdn_accept_workspace_bytes",
+    "gdn_accept_sampled_noalloc",
+    "gdn_accept_noalloc_max_bytes",
     "gdn_accept_greedy",
     "gdn_accept_sampled",
     "gdn_history_rewind",
@@ -99,6 +101,10 @@ def _load() -> ctypes.CDLL:
     lib.gdn_accept_greedy.argtypes = [vp, ctypes.c_int, vp, ap, vp, vp, vp, sz, vp]
     lib.gdn_accept_sampled.restype = ctypes.c_int
     lib.gdn_accept_sampled.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp, ctypes.c_float, ap, vp, vp, vp, sz, vp]
+    lib.gdn_accept_sampled_noalloc.restype = ctypes.c_int
+    lib.gdn_accept_sampled_noalloc.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp, ctypes.c_float, ap, vp, vp, vp]
+    lib.gdn_accept_noalloc_max_bytes.restype = sz
+    lib.gdn_accept_noalloc_max_bytes.argtypes = []
     lib.gdn_history_rewind.restype = ctypes.c_int
     lib.gdn_history_rewind.argtypes = [vp, vp, vp, i32, i32, i32, i32, ctypes.c_int, vp]
     mp = ctypes.POINTER(gdn_mixer_inputs)
@@ -325,6 +331,29 @@ def gdn_accept_sampled(target_logits, draft_logits, draft_tokens, u_accept, u_sa
                                 _ptr(next_token), _ptr(ws), nb, _stream(stream))
     if rc != 0:
         raise GdnError(rc, "gdn_accept_sampled")
+
+
+def gdn_accept_sampled_noalloc(target_logits, draft_logits, draft_tokens, u_accept, u_sample, temperature, n_out,
+                               next_token, stream=None) -> None:
+    """gdn_accept_sampled with the library's own per-device scratch instead of a
+    workspace: allocates nothing (see gdn_accept_sampled_noalloc in
+    include/gdn.h; calls that overlap on one device race)."""
+    shp = _accept_shape(target_logits)
+    _check_accept(shp, draft_tokens, n_out, next_token)
+    B, T, V = shp.B, shp.T, shp.V
+    if T > 1:
+        if tuple(draft_logits.shape) != (B, T - 1, V) or draft_logits.dtype != target_logits.dtype:
+            raise ValueError("draft_logits must be [B][T-1][V] in the target logits' dtype")
+        if tuple(u_accept.shape) != (B, T - 1) or u_accept.dtype != torch.float32:
+            raise ValueError("u_accept must be float32 [B][T-1]")
+    if tuple(u_sample.shape) != (B,) or u_sample.dtype != torch.float32:
+        raise ValueError("u_sample must be float32 [B]")
+    rc = lib.gdn_accept_sampled_noalloc(_ptr(target_logits), _ptr(draft_logits if T > 1 else None),
+                                        _dt(target_logits), _ptr(draft_tokens if T > 1 else None),
+                                        _ptr(u_accept if T > 1 else None), _ptr(u_sample), float(temperature),
+                                        ctypes.byref(shp), _ptr(n_out), _ptr(next_token), _stream(stream))
+    if rc != 0:
+        raise GdnError(rc, "gdn_accept_sampled_noalloc")
 
 
 def gdn_history_rewind(history, rows, n, stream=None) -> None:

@@ -163,6 +163,22 @@ def test_accept_and_rewind_reject_bad_arguments(G):
     assert L.gdn_accept_workspace_bytes(_ashape(), 1) > L.gdn_accept_workspace_bytes(_ashape(), 0) > 0
     assert L.gdn_accept_workspace_bytes(_ashape(T=0), 0) == 0
 
+    # The call without a workspace: the same checks; a shape whose workspace
+    # exceeds the library's per-device scratch is refused before any device work.
+    def noalloc(temp=1.0, draft=FAKE, shp=None, n=FAKE):
+        return L.gdn_accept_sampled_noalloc(FAKE, draft, 1, FAKE, FAKE, FAKE, temp, shp or _ashape(), n, FAKE,
+                                            None)
+
+    cap = L.gdn_accept_noalloc_max_bytes()
+    assert cap == 1 << 20
+    assert noalloc(temp=0.0) == -3 and noalloc(temp=float("nan")) == -3
+    assert noalloc(draft=None) == -1 and noalloc(n=ctypes.c_void_p((1 << 20) + 2)) == -1
+    assert noalloc(shp=_ashape(B=0)) == -2 and noalloc(shp=_ashape(T=17)) == -3
+    fits = _ashape(B=96, T=8, V=151936)
+    over = _ashape(B=128, T=8, V=151936)
+    assert L.gdn_accept_workspace_bytes(fits, 1) <= cap < L.gdn_accept_workspace_bytes(over, 1)
+    assert noalloc(shp=over) == -4
+
     def rewind(B=1, W=3, T=8, C=16, dt=1, hist=FAKE):
         return L.gdn_history_rewind(hist, FAKE, FAKE, B, W, T, C, dt, None)
 
