@@ -1141,6 +1141,398 @@ __global__ __launch_bounds__(512) void prefill_prep_kernel(
     prep_role<DK, 8>(sm, blockIdx.x, gridDim.x, q, k, g, beta, L, H, heads, nchunks, pbeg, pend, ws);
 }
 
+// ---------------------------------------------------------------------------
+// One pass, many heads (dv = 128): one workgroup of 4 waves per (instance, head),
+// wave w owning value rows 32 w .. 32 w + 31 over all keys, so the state-coupled
+// products need no exchange between waves.  76 KB of LDS, so two heads share a
+// compute unit and one head's chunk chain runs in the other's latency shadows.
+// Per chunk:
+//   P0  K and Q copied global -> LDS (swizzled rows), gates by wave 0;
+//   P1  Gram tiles: A = strictly-lower(beta Gamma K K^T) in fp32, P = lower-incl
+//       (Gamma Q K^T) split into bf16 hi/lo straight from the MFMA tiles;
+//   P2  Linv = (I + A)^{-1} in place over A;
+//   P3  Linv split into bf16 hi/lo, in place over A (read, barrier, write);
+//   P4  X = K S^T, Y = Q S^T, R, D = Linv R, O = diag(gamma) Y + P D and
+//       S <- gamma_last S + K^T diag(e) D for the wave's 32 rows.
+// Operands follow the scan's mapping (tau token order, st[kt][r] = key
+// 32 (kt/2) + 8 lg + 4 (kt%2) + r), with two 16-row tiles per wave.
+// ---------------------------------------------------------------------------
+template <int DK>
+struct alignas(16) PassLds {
+    uint8_t K[C * DK * 2];
+    uint8_t Q[C * DK * 2];
+    uint8_t PM[2 * C * C * 2];         // P hi, P lo
+    union {
+        float A[C][C + 4];             // A, then Linv in place (P1 - P3)
+        uint8_t Li[2 * C * C * 2];     // Linv hi, Linv lo (P3 - P4)
+    };
+    float scr[4 * 640];                // the inverse's scratch
+    float G[C], gam[C], ee[C], bet[C];
+};
+
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
+template <int DK>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_pass_kernel(
+    float *__restrict__ S, const __hip_bfloat16 *__restrict__ q, const __hip_bfloat16 *__restrict__ k,
+    const __hip_bfloat16 *__restrict__ v, const float *__restrict__ g, const float *__restrict__ beta, int L,
+    int H, float *__restrict__ o) {
+    constexpr int DV = 128, NW = 4;
+    constexpr int KT = DK / 16, KB = DK / 32;
+    constexpr int NKQ = C * DK * 2 / 1024;   // 1 KiB blocks of a key or query chunk
+    constexpr int RPB = 1024 / (2 * DK);     // rows per block
+    static_assert(NKQ % NW == 0, "every wave copies the same number of blocks");
+    __shared__ PassLds<DK> sm;
+
+    const int bh = blockIdx.x, b = bh / H, h = bh - b * H;
+    const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int irow[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) irow[rt] = 32 * w + 16 * rt + lr;
+
+    // State: st[rt][kt][r] = S[irow[rt]][32 (kt/2) + 8 lg + 4 (kt%2) + r].
+    float st[2][KT][4];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+        const float *Srow = S + (size_t(bh) * DV + irow[rt]) * DK;
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+            const float4 s4 = *reinterpret_cast<const float4 *>(Srow + 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1));
+            st[rt][kt][0] = s4.x;
+            st[rt][kt][1] = s4.y;
+            st[rt][kt][2] = s4.z;
+            st[rt][kt][3] = s4.w;
+        }
+    }
+    // P's strictly upper 16x16 tiles inside its diagonal 32x32 blocks are read as
+    // operands (p <= tt / 2) and never computed: zero once (hi and lo).
+    if (tid < 128) {
+        const int arr = tid >> 6, i = tid & 63, blk = i >> 5, t = 32 * blk + ((i >> 1) & 15);
+        const int piece = 4 * blk + 2 + (i & 1);
+        *reinterpret_cast<uint4 *>(sm.PM + mat_off(arr, t, piece)) = make_uint4(0u, 0u, 0u, 0u);
+    }
+
+    const size_t kstride = size_t(H) * DK, vstride = size_t(H) * DV;
+    const uint32_t kstride_b = uint32_t(kstride) * 2;
+    const __hip_bfloat16 *kb = k + (size_t(b) * L * H + h) * DK;
+    const __hip_bfloat16 *qb = q + (size_t(b) * L * H + h) * DK;
+    const uint16_t *vbase = reinterpret_cast<const uint16_t *>(v) + (size_t(b) * L * H + h) * DV;
+    auto kq_piece = [&](int blk) {
+        const int row = blk * RPB + lane / (64 / RPB), slot = lane % (64 / RPB);
+        return DK == 128 ? (slot ^ swz16(row)) : (slot ^ swz8(row));
+    };
+    uint32_t vo_kq[NKQ / NW];
+#pragma unroll
+    for (int u = 0; u < NKQ / NW; ++u)
+        vo_kq[u] = uint32_t(lane / (64 / RPB)) * kstride_b + 16u * uint32_t(kq_piece(NW * u + w));
+    const uint32_t lk = lds_addr(sm.K), lq = lds_addr(sm.Q);
+
+    // Per-lane LDS offsets of the P4 operands (aKQ, aM, aTR, set per chunk).  In
+    // the tau order a result tile's token is t = T(tt) + tl, T(tt) = 32 (tt/2) +
+    // 4 (tt%2) a constant and tl = 8 (lr/4) + lr%4 the lane's part, and every
+    // swizzle term depends on tl alone: an operand address is a per-lane offset
+    // (one per contraction block) plus a compile-time constant, which the LDS
+    // instructions take as their immediate offset.  Likewise the K^T reads of the
+    // state update (rows ta = 32 p + 8 lg + lr/4, + 4; piece 4 (kt/2) + lr%4):
+    // the swizzle of ta depends on tal = 8 lg + lr/4 alone.
+    auto Tc = [](int tt) { return 32 * (tt >> 1) + 4 * (tt & 1); };
+
+    const int nchunks = (L + C - 1) / C;
+    for (int c = 0; c < nchunks; ++c) {
+        const int c0 = c * C, n = min(C, L - c0);
+        const size_t row0 = size_t(b) * L + c0;
+        // The lane index made opaque per chunk: the per-lane addresses below are
+        // recomputed each chunk (a few VALU) rather than held across the loop.
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int lr = ln & 15, lg = ln >> 4;
+        const int irow[2] = {32 * w + lr, 32 * w + 16 + lr};
+        const int tl = 8 * (lr >> 2) + (lr & 3), tal = 8 * lg + (lr >> 2);
+        uint32_t aKQ[KB], aM[2], aTR[KT / 2];
+#pragma unroll
+        for (int p = 0; p < KB; ++p) aKQ[p] = kq_off<DK>(tl, 4 * p + lg);
+#pragma unroll
+        for (int p = 0; p < 2; ++p) aM[p] = mat_off(0, tl, 4 * p + lg);
+#pragma unroll
+        for (int kk = 0; kk < KT / 2; ++kk) aTR[kk] = kq_off<DK>(tal, 4 * kk + (lr & 3));
+        // P0: gates' inputs, the chunk's keys and queries into LDS.
+        float gt = 0.f, bt = 0.f;
+        if (w == 0) {
+            const size_t gi = (row0 + min(lane, n - 1)) * H + h;
+            gt = g[gi];
+            bt = beta[gi];
+        }
+        asm volatile("" ::: "memory");
+        if (n == C) {
+            const uint8_t *kc = reinterpret_cast<const uint8_t *>(kb + size_t(c0) * kstride);
+            const uint8_t *qc = reinterpret_cast<const uint8_t *>(qb + size_t(c0) * kstride);
+#pragma unroll
+            for (int u = 0; u < NKQ / NW; ++u) {
+                const int blk = NW * u + w;
+                const size_t boff = size_t(blk * RPB) * kstride_b;
+                dma16s_nt(kc + boff, vo_kq[u], lk + blk * 1024);
+                dma16s_nt(qc + boff, vo_kq[u], lq + blk * 1024);
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < NKQ / NW; ++u) {
+                const int blk = NW * u + w, row = blk * RPB + lane / (64 / RPB);
+                const size_t off = size_t(min(c0 + row, L - 1)) * kstride + 8 * kq_piece(blk);
+                dma16_nt(kb + off, lk + blk * 1024);
+                dma16_nt(qb + off, lq + blk * 1024);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0): the copies (and the gate inputs) have landed
+        asm volatile("" ::: "memory");
+        if (w == 0) chunk_gates(sm, gt, bt, n, lane);
+        __syncthreads();
+
+        // This wave's value columns, for P4: vr[rt][p][hh][r/2][r%2] = v[t][irow[rt]]
+        // with t = 32 p + 8 lg + 4 hh + r (rows past the prompt read the last row).
+        u16x2 vr[2][2][2][2];
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = min(32 * p + 8 * lg + 4 * hh + r, n - 1);
+#pragma unroll
+                    for (int rt = 0; rt < 2; ++rt)
+                        vr[rt][p][hh][r >> 1][r & 1] =
+                            __builtin_nontemporal_load(vbase + size_t(c0 + t) * vstride + irow[rt]);
+                }
+
+        // P1: Gram tiles (five per wave): A from K K^T, P from Q K^T, lower tiles.
+#pragma unroll 1
+        for (int qi = w; qi < 20; qi += NW) {
+            const bool isq = qi >= 10;
+            const int pq = isq ? qi - 10 : qi;
+            const int tt = pq >= 6 ? 3 : pq >= 3 ? 2 : pq >= 1 ? 1 : 0;
+            const int jt = pq - tt * (tt + 1) / 2;
+            const uint8_t *Ab = isq ? sm.Q : sm.K;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb2 = 0; kb2 < KB; ++kb2)
+                acc = mma(lds16(Ab + kq_off<DK>(16 * tt + lr, 4 * kb2 + lg)),
+                          lds16(sm.K + kq_off<DK>(16 * jt + lr, 4 * kb2 + lg)), acc);
+            const int j = 16 * jt + lr;
+            const float Gj = sm.G[j];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * tt + 4 * lg + r;
+                const float dec = __expf(sm.G[t] - Gj);
+                if (!isq) {
+                    sm.A[t][j] = j < t ? sm.bet[t] * dec * acc[r] : 0.f;
+                } else {
+                    const float pv = j <= t ? dec * acc[r] : 0.f;
+                    const __bf16 hi = static_cast<__bf16>(pv);
+                    const __bf16 lo = static_cast<__bf16>(pv - static_cast<float>(hi));
+                    const int off = mat_off(0, t, j >> 3) + 2 * (j & 7);
+                    *reinterpret_cast<__bf16 *>(sm.PM + off) = hi;
+                    *reinterpret_cast<__bf16 *>(sm.PM + off + C * C * 2) = lo;
+                }
+            }
+        }
+        __syncthreads();   // A and P complete
+
+        // P2: Linv = (I + A)^{-1} in place (each block is read before it is overwritten).
+        tri_inverse(sm.A, sm.A, sm.scr, w, ln, [] {});
+        // P3: Linv split into hi/lo (zero in the strictly upper blocks), in place.
+        Split8 lsp[C * C / 8 / 256];
+#pragma unroll
+        for (int u = 0; u < C * C / 8 / 256; ++u) {
+            const int idx = tid + 256 * u, t = idx / (C / 8), j8 = (idx - t * (C / 8)) * 8;
+            float a[8];
+            *reinterpret_cast<float4 *>(a) = *reinterpret_cast<const float4 *>(&sm.A[t][j8]);
+            *reinterpret_cast<float4 *>(a + 4) = *reinterpret_cast<const float4 *>(&sm.A[t][j8 + 4]);
+            if ((j8 >> 4) > (t >> 4)) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) a[e] = 0.f;
+            }
+            lsp[u] = split8(a);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < C * C / 8 / 256; ++u) {
+            const int idx = tid + 256 * u, t = idx / (C / 8), j8 = (idx - t * (C / 8)) * 8;
+            *reinterpret_cast<bf16x8 *>(sm.Li + mat_off(0, t, j8 >> 3)) = lsp[u].hi;
+            *reinterpret_cast<bf16x8 *>(sm.Li + mat_off(1, t, j8 >> 3)) = lsp[u].lo;
+        }
+        __syncthreads();
+
+        // P4: the wave's state-coupled products.  X = K S^T and Y = Q S^T.
+        f32x4 X[2][4], Y[2][4];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) X[rt][tt] = Y[rt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int p = 0; p < KB; ++p) {
+            Split8 sB[2];
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                const float x[8] = {st[rt][2 * p][0], st[rt][2 * p][1], st[rt][2 * p][2], st[rt][2 * p][3],
+                                    st[rt][2 * p + 1][0], st[rt][2 * p + 1][1], st[rt][2 * p + 1][2],
+                                    st[rt][2 * p + 1][3]};
+                sB[rt] = split8(x);
+            }
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                const int toff = Tc(tt) * 2 * DK;
+                const bf16x8 ka = lds16(sm.K + aKQ[p] + toff);
+                const bf16x8 qa = lds16(sm.Q + aKQ[p] + toff);
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt) {
+                    X[rt][tt] = mma(ka, sB[rt].hi, X[rt][tt]);
+                    X[rt][tt] = mma(ka, sB[rt].lo, X[rt][tt]);
+                    Y[rt][tt] = mma(qa, sB[rt].hi, Y[rt][tt]);
+                    Y[rt][tt] = mma(qa, sB[rt].lo, Y[rt][tt]);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // Gates of the lane's tokens t0 .. t0 + 3, t0 = 32 p + 8 lg + 4 hh, read where used.
+        auto gate4 = [&](const float *arr, int p, int hh) {
+            return *reinterpret_cast<const float4 *>(arr + 32 * p + 8 * lg + 4 * hh);
+        };
+        // R = diag(beta) (V - diag(gamma) X), split as the B operand of D = Linv R.
+        Split8 rB[2][2];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            float4 ga[2], be[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                ga[hh] = gate4(sm.gam, p, hh);
+                be[hh] = gate4(sm.bet, p, hh);
+            }
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                float x[8];
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        x[4 * hh + r] = (&be[hh].x)[r] * (bf16_bits_to_f32(vr[rt][p][hh][r >> 1][r & 1]) -
+                                                         (&ga[hh].x)[r] * X[rt][2 * p + hh][r]);
+                rB[rt][p] = split8(x);
+            }
+        }
+        // D = Linv R (p <= tt / 2).
+        f32x4 D[2][4];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            D[0][tt] = D[1][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int p = 0; p <= tt / 2; ++p) {
+                Split8 li;
+                li.hi = lds16(sm.Li + aM[p] + Tc(tt) * 128);
+                li.lo = lds16(sm.Li + aM[p] + Tc(tt) * 128 + C * C * 2);
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt) D[rt][tt] = mma3(li, rB[rt][p], D[rt][tt]);
+            }
+        }
+        // O = diag(gamma) Y + P D, stored for tokens < n (D split as is).
+        {
+            Split8 dB[2][2];
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int p = 0; p < 2; ++p) {
+                    float x[8];
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) x[4 * hh + r] = D[rt][2 * p + hh][r];
+                    dB[rt][p] = split8(x);
+                }
+            float *orow = o + (row0 * H + h) * DV;
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                const float4 ga = gate4(sm.gam, tt >> 1, tt & 1);
+                f32x4 Ot[2] = {Y[0][tt], Y[1][tt]};
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) Ot[rt][r] *= (&ga.x)[r];
+#pragma unroll
+                for (int p = 0; p <= tt / 2; ++p) {
+                    Split8 pm;
+                    pm.hi = lds16(sm.PM + aM[p] + Tc(tt) * 128);
+                    pm.lo = lds16(sm.PM + aM[p] + Tc(tt) * 128 + C * C * 2);
+#pragma unroll
+                    for (int rt = 0; rt < 2; ++rt) Ot[rt] = mma3(pm, dB[rt][p], Ot[rt]);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int tr = 32 * (tt >> 1) + 8 * lg + 4 * (tt & 1) + r;
+                    if (tr < n) {
+#pragma unroll
+                        for (int rt = 0; rt < 2; ++rt)
+                            __builtin_nontemporal_store(Ot[rt][r], orow + size_t(tr) * vstride + irow[rt]);
+                    }
+                }
+            }
+        }
+        // D scaled by e and split, for the state update.
+        Split8 eB[2][2];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            float4 ee[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) ee[hh] = gate4(sm.ee, p, hh);
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                float y[8];
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) y[4 * hh + r] = (&ee[hh].x)[r] * D[rt][2 * p + hh][r];
+                eB[rt][p] = split8(y);
+            }
+        }
+        const float glast = sm.gam[n - 1];
+        // S <- gamma_last S + K^T diag(e) D.
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+            const int h8 = (kt & 1) << 3;
+            bf16x8 kta[2];
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                const uint8_t *base = sm.K + aTR[kt >> 1] + 32 * p * 2 * DK + h8;
+                kta[p] = cat4(read_tr(base), read_tr(base + 4 * 2 * DK));
+            }
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                f32x4 U = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int p = 0; p < 2; ++p) {
+                    U = mma(kta[p], eB[rt][p].hi, U);
+                    U = mma(kta[p], eB[rt][p].lo, U);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) st[rt][kt][r] = glast * st[rt][kt][r] + U[r];
+            }
+        }
+        __syncthreads();   // the next chunk's copies overwrite K, Q and the matrices
+    }
+
+    {
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int lr = ln & 15, lg = ln >> 4;
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            float *Srow = S + (size_t(bh) * DV + 32 * w + 16 * rt + lr) * DK;
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt)
+                *reinterpret_cast<float4 *>(Srow + 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1)) =
+                    make_float4(st[rt][kt][0], st[rt][kt][1], st[rt][kt][2], st[rt][kt][3]);
+        }
+    }
+}
+
 template <int DK, int DV>
 hipError_t launch_dk_dv(float *S, const void *q, const void *k, const void *v, const float *g,
                         const float *beta, int L, const gdn_shape &s, float *o, void *ws,
@@ -1191,8 +1583,13 @@ hipError_t launch_dk_dv(float *S, const void *q, const void *k, const void *v, c
         return hipSuccess;
     }
     // One pass: one workgroup per head.
-    hipLaunchKernelGGL((prefill_kernel<DK, DV, DV / 16>), dim3(unsigned(heads)), dim3(4 * DV), 0, st,
-                       S, qq, kk, vv, g, beta, L, s.H, o);
+    if constexpr (DV == 128) {
+        hipLaunchKernelGGL((prefill_pass_kernel<DK>), dim3(unsigned(heads)), dim3(256), 0, st, S, qq, kk, vv, g,
+                           beta, L, s.H, o);
+    } else {
+        hipLaunchKernelGGL((prefill_kernel<DK, DV, DV / 16>), dim3(unsigned(heads)), dim3(4 * DV), 0, st,
+                           S, qq, kk, vv, g, beta, L, s.H, o);
+    }
     return hipGetLastError();
 }
 

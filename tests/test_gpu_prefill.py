@@ -220,3 +220,24 @@ def test_prefill_both_schedules(G, schedule, dk, dv, L):
     assert not torch.isnan(o).any()
     assert rel_err_outputs(o, ref_o) <= OUT_TOL
     assert rel_err_state(S, ref_S) <= STATE_TOL
+
+
+@pytest.mark.parametrize("dk", [128, 64])
+@pytest.mark.parametrize("L", [1, 64, 65, 200])
+def test_prefill_one_pass_many_heads(G, dk, L):
+    """256 (instance, head) pairs take the one-pass kernel (a workgroup per head,
+    two heads per compute unit): every output and the final state against the
+    sequential oracle, with full and partial last chunks."""
+    B, H, dv = 8, 32, 128
+    print_case(test="prefill_one_pass_many", B=B, H=H, dk=dk, dv=dv, L=L, seed=41 + L)
+    x = make_inputs(B, H, dk, dv, L, seed=41 + L, device=DEV)
+    xc = x.to("cpu")
+    assert G.gdn_prefill_workspace_bytes(x.S0, L) == 0
+    o = torch.full((B, L, H, dv), float("nan"), dtype=torch.float32, device=DEV)
+    S = x.S0.clone()
+    G.gdn_prefill_chunked(S, x.q, x.k, x.v, x.g, x.beta, o)
+    torch.cuda.synchronize()
+    ref_o, ref_S = oracle.prefill_seq(xc.S0, xc.q, xc.k, xc.v, xc.g, xc.beta)
+    assert not torch.isnan(o).any()
+    assert rel_err_outputs(o, ref_o) <= OUT_TOL
+    assert rel_err_state(S, ref_S) <= STATE_TOL
