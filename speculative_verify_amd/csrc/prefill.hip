@@ -1149,18 +1149,23 @@ __global__ __launch_bounds__(512) void prefill_prep_kernel(
 // Per chunk:
 //   P0  K and Q copied global -> LDS (swizzled rows), gates by wave 0;
 //   P1  Gram tiles: A = strictly-lower(beta Gamma K K^T) in fp32, P = lower-incl
-//       (Gamma Q K^T) split into bf16 hi/lo straight from the MFMA tiles;
-//   P2  Linv = (I + A)^{-1} in place over A;
+//       (Gamma Q K^T) split into bf16 hi/lo straight from the MFMA tiles (a row
+//       band of each per wave); Y = Q S^T for the wave's 32 rows;
+//   P2  the chunk's values copied into Q's space; Linv = (I + A)^{-1} in place
+//       over A;
 //   P3  Linv split into bf16 hi/lo, in place over A (read, barrier, write);
-//   P4  X = K S^T, Y = Q S^T, R, D = Linv R, O = diag(gamma) Y + P D and
-//       S <- gamma_last S + K^T diag(e) D for the wave's 32 rows.
+//   P4  X = K S^T, R (values by transposed LDS reads), D = Linv R,
+//       O = diag(gamma) Y + P D and S <- gamma_last S + K^T diag(e) D.
 // Operands follow the scan's mapping (tau token order, st[kt][r] = key
 // 32 (kt/2) + 8 lg + 4 (kt%2) + r), with two 16-row tiles per wave.
 // ---------------------------------------------------------------------------
 template <int DK>
 struct alignas(16) PassLds {
     uint8_t K[C * DK * 2];
-    uint8_t Q[C * DK * 2];
+    union {
+        uint8_t Q[C * DK * 2];         // queries (P0 - P1)
+        uint8_t V[C * 128 * 2];        // then the chunk's values, [t][dv = 128] (P2 - P4)
+    };
     uint8_t PM[2 * C * C * 2];         // P hi, P lo
     union {
         float A[C][C + 4];             // A, then Linv in place (P1 - P3)
@@ -1205,14 +1210,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
             st[rt][kt][3] = s4.w;
         }
     }
-    // P's strictly upper 16x16 tiles inside its diagonal 32x32 blocks are read as
-    // operands (p <= tt / 2) and never computed: zero once (hi and lo).
-    if (tid < 128) {
-        const int arr = tid >> 6, i = tid & 63, blk = i >> 5, t = 32 * blk + ((i >> 1) & 15);
-        const int piece = 4 * blk + 2 + (i & 1);
-        *reinterpret_cast<uint4 *>(sm.PM + mat_off(arr, t, piece)) = make_uint4(0u, 0u, 0u, 0u);
-    }
-
     const size_t kstride = size_t(H) * DK, vstride = size_t(H) * DV;
     const uint32_t kstride_b = uint32_t(kstride) * 2;
     const __hip_bfloat16 *kb = k + (size_t(b) * L * H + h) * DK;
@@ -1226,7 +1223,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 #pragma unroll
     for (int u = 0; u < NKQ / NW; ++u)
         vo_kq[u] = uint32_t(lane / (64 / RPB)) * kstride_b + 16u * uint32_t(kq_piece(NW * u + w));
-    const uint32_t lk = lds_addr(sm.K), lq = lds_addr(sm.Q);
+    const uint32_t lk = lds_addr(sm.K), lq = lds_addr(sm.Q), lv = lds_addr(sm.V);
+    const uint32_t vstride_b = uint32_t(vstride) * 2;
+    const uint32_t vo_v = uint32_t(lane >> 4) * vstride_b + 16u * uint32_t(lane & 15);   // V copies: row, piece
 
     // Per-lane LDS offsets of the P4 operands (aKQ, aM, aTR, set per chunk).  In
     // the tau order a result tile's token is t = T(tt) + tl, T(tt) = 32 (tt/2) +
@@ -1259,7 +1258,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         // P0: gates' inputs, the chunk's keys and queries into LDS.
         float gt = 0.f, bt = 0.f;
         if (w == 0) {
-            const size_t gi = (row0 + min(lane, n - 1)) * H + h;
+            const size_t gi = (row0 + min(ln, n - 1)) * H + h;
             gt = g[gi];
             bt = beta[gi];
         }
@@ -1288,54 +1287,100 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         if (w == 0) chunk_gates(sm, gt, bt, n, lane);
         __syncthreads();
 
-        // This wave's value columns, for P4: vr[rt][p][hh][r/2][r%2] = v[t][irow[rt]]
-        // with t = 32 p + 8 lg + 4 hh + r (rows past the prompt read the last row).
-        u16x2 vr[2][2][2][2];
-#pragma unroll
-        for (int p = 0; p < 2; ++p)
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = min(32 * p + 8 * lg + 4 * hh + r, n - 1);
-#pragma unroll
-                    for (int rt = 0; rt < 2; ++rt)
-                        vr[rt][p][hh][r >> 1][r & 1] =
-                            __builtin_nontemporal_load(vbase + size_t(c0 + t) * vstride + irow[rt]);
-                }
 
-        // P1: Gram tiles (five per wave): A from K K^T, P from Q K^T, lower tiles.
-#pragma unroll 1
-        for (int qi = w; qi < 20; qi += NW) {
-            const bool isq = qi >= 10;
-            const int pq = isq ? qi - 10 : qi;
-            const int tt = pq >= 6 ? 3 : pq >= 3 ? 2 : pq >= 1 ? 1 : 0;
-            const int jt = pq - tt * (tt + 1) / 2;
-            const uint8_t *Ab = isq ? sm.Q : sm.K;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        // P1: Gram tiles, transposed so that a lane holds four consecutive j of one
+        // t: wave w takes row band tt = w of A (from K K^T) and row band 3 - w of P
+        // (from Q K^T), all four tiles of each (the masks zero what lies above the
+        // diagonal), written as one 16-byte store of A[t][j .. j + 3] and two 8-byte
+        // stores of P's hi and lo parts per tile.
+        {
+            const int ta = 16 * w + lr, tp = 16 * (3 - w) + lr;   // the lane's t in each band
+            f32x4 aT[4], pT[4];
 #pragma unroll
-            for (int kb2 = 0; kb2 < KB; ++kb2)
-                acc = mma(lds16(Ab + kq_off<DK>(16 * tt + lr, 4 * kb2 + lg)),
-                          lds16(sm.K + kq_off<DK>(16 * jt + lr, 4 * kb2 + lg)), acc);
-            const int j = 16 * jt + lr;
-            const float Gj = sm.G[j];
+            for (int jt = 0; jt < 4; ++jt) aT[jt] = pT[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * tt + 4 * lg + r;
-                const float dec = __expf(sm.G[t] - Gj);
-                if (!isq) {
-                    sm.A[t][j] = j < t ? sm.bet[t] * dec * acc[r] : 0.f;
-                } else {
-                    const float pv = j <= t ? dec * acc[r] : 0.f;
-                    const __bf16 hi = static_cast<__bf16>(pv);
-                    const __bf16 lo = static_cast<__bf16>(pv - static_cast<float>(hi));
-                    const int off = mat_off(0, t, j >> 3) + 2 * (j & 7);
-                    *reinterpret_cast<__bf16 *>(sm.PM + off) = hi;
-                    *reinterpret_cast<__bf16 *>(sm.PM + off + C * C * 2) = lo;
+            for (int kb2 = 0; kb2 < KB; ++kb2) {
+                const bf16x8 kt_b = lds16(sm.K + kq_off<DK>(ta, 4 * kb2 + lg));
+                const bf16x8 qt_b = lds16(sm.Q + kq_off<DK>(tp, 4 * kb2 + lg));
+#pragma unroll
+                for (int jt = 0; jt < 4; ++jt) {
+                    const bf16x8 kj = lds16(sm.K + kq_off<DK>(16 * jt + lr, 4 * kb2 + lg));
+                    aT[jt] = mma(kj, kt_b, aT[jt]);
+                    pT[jt] = mma(kj, qt_b, pT[jt]);
                 }
             }
+            const float Gta = sm.G[ta], Gtp = sm.G[tp], bta = sm.bet[ta];
+#pragma unroll
+            for (int jt = 0; jt < 4; ++jt) {
+                const int j0 = 16 * jt + 4 * lg;
+                const float4 Gj = *reinterpret_cast<const float4 *>(&sm.G[j0]);
+                float av[4], pv[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int j = j0 + r;
+                    av[r] = j < ta ? bta * __expf(Gta - (&Gj.x)[r]) * aT[jt][r] : 0.f;
+                    pv[r] = j <= tp ? __expf(Gtp - (&Gj.x)[r]) * pT[jt][r] : 0.f;
+                }
+                *reinterpret_cast<float4 *>(&sm.A[ta][j0]) = make_float4(av[0], av[1], av[2], av[3]);
+                typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+                typedef float f32x2 __attribute__((ext_vector_type(2)));
+                uint32_t hi[2], lo[2];
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const uint32_t u = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{pv[2 * i], pv[2 * i + 1]}), bf16x2));
+                    hi[i] = u;
+                    const float h0 = __uint_as_float(u << 16), h1 = __uint_as_float(u & 0xffff0000u);
+                    lo[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{pv[2 * i] - h0, pv[2 * i + 1] - h1}), bf16x2));
+                }
+                const int off = mat_off(0, tp, j0 >> 3) + 2 * (j0 & 7);
+                *reinterpret_cast<uint2 *>(sm.PM + off) = make_uint2(hi[0], hi[1]);
+                *reinterpret_cast<uint2 *>(sm.PM + off + C * C * 2) = make_uint2(lo[0], lo[1]);
+            }
         }
-        __syncthreads();   // A and P complete
+        // Y = Q S^T for the wave's two row tiles (tau token order): Q's last use.
+        f32x4 Y[2][4];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) Y[rt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int p = 0; p < KB; ++p) {
+            Split8 sB[2];
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                const float x[8] = {st[rt][2 * p][0], st[rt][2 * p][1], st[rt][2 * p][2], st[rt][2 * p][3],
+                                    st[rt][2 * p + 1][0], st[rt][2 * p + 1][1], st[rt][2 * p + 1][2],
+                                    st[rt][2 * p + 1][3]};
+                sB[rt] = split8(x);
+            }
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                const bf16x8 qa = lds16(sm.Q + aKQ[p] + Tc(tt) * 2 * DK);
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt) {
+                    Y[rt][tt] = mma(qa, sB[rt].hi, Y[rt][tt]);
+                    Y[rt][tt] = mma(qa, sB[rt].lo, Y[rt][tt]);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __syncthreads();   // A and P complete; Q is dead
+        // The chunk's values into Q's space (V), [t][DV] bf16 rows (block = 4
+        // rows), landing while the inverse runs.
+        if (n == C) {
+            const uint8_t *vc = reinterpret_cast<const uint8_t *>(vbase + size_t(c0) * vstride);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int blk = NW * u + w;
+                dma16s_nt(vc + size_t(4 * blk) * vstride_b, vo_v, lv + blk * 1024);
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int blk = NW * u + w, row = 4 * blk + (ln >> 4);
+                dma16_nt(vbase + size_t(min(c0 + row, L - 1)) * vstride + 8 * (ln & 15), lv + blk * 1024);
+            }
+        }
 
         // P2: Linv = (I + A)^{-1} in place (each block is read before it is overwritten).
         tri_inverse(sm.A, sm.A, sm.scr, w, ln, [] {});
@@ -1362,12 +1407,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         }
         __syncthreads();
 
-        // P4: the wave's state-coupled products.  X = K S^T and Y = Q S^T.
-        f32x4 X[2][4], Y[2][4];
+        // P4: the wave's state-coupled products.  X = K S^T.
+        f32x4 X[2][4];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt) X[rt][tt] = Y[rt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int tt = 0; tt < 4; ++tt) X[rt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int p = 0; p < KB; ++p) {
             Split8 sB[2];
@@ -1380,19 +1425,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
             }
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
-                const int toff = Tc(tt) * 2 * DK;
-                const bf16x8 ka = lds16(sm.K + aKQ[p] + toff);
-                const bf16x8 qa = lds16(sm.Q + aKQ[p] + toff);
+                const bf16x8 ka = lds16(sm.K + aKQ[p] + Tc(tt) * 2 * DK);
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt) {
                     X[rt][tt] = mma(ka, sB[rt].hi, X[rt][tt]);
                     X[rt][tt] = mma(ka, sB[rt].lo, X[rt][tt]);
-                    Y[rt][tt] = mma(qa, sB[rt].hi, Y[rt][tt]);
-                    Y[rt][tt] = mma(qa, sB[rt].lo, Y[rt][tt]);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+        // The chunk's values have landed in Q's space (every wave's copies).
+        __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0)
+        __syncthreads();
         // Gates of the lane's tokens t0 .. t0 + 3, t0 = 32 p + 8 lg + 4 hh, read where used.
         auto gate4 = [&](const float *arr, int p, int hh) {
             return *reinterpret_cast<const float4 *>(arr + 32 * p + 8 * lg + 4 * hh);
@@ -1409,12 +1453,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
             }
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt) {
+                // v[t0 .. t0 + 3][irow[rt]] by one transposed read (V rows are 2 DV bytes).
+                bf16x4 vt[2];
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int t0 = 32 * p + 8 * lg + 4 * hh;
+                    vt[hh] = read_tr(sm.V + (t0 + (lr >> 2)) * 2 * DV + 2 * (32 * w + 16 * rt) + 8 * (lr & 3));
+                }
                 float x[8];
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        x[4 * hh + r] = (&be[hh].x)[r] * (bf16_bits_to_f32(vr[rt][p][hh][r >> 1][r & 1]) -
+                        x[4 * hh + r] = (&be[hh].x)[r] * (static_cast<float>(vt[hh][r]) -
                                                          (&ga[hh].x)[r] * X[rt][2 * p + hh][r]);
                 rB[rt][p] = split8(x);
             }
