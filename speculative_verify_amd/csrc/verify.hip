@@ -145,8 +145,17 @@ __device__ inline float wave_sum(float v) {
 //
 // MIX: q, k, v and the gates come from the mixer's raw inputs (`mix`) instead of
 // q, k, v, g, beta, and the outputs are the gated RMS norm of the recurrence's.
+// Occupancy: three waves a SIMD (168 VGPRs) hold the 48-layer state in one round
+// of register-resident slices; fp32 inputs (the small-shape path: 8-element
+// operand rows and fp32 MFMA operands take more registers) get two (256 VGPRs),
+// which keeps them free of scratch spills.
+template <typename TIn>
+constexpr int verify_waves_per_eu() {
+    return sizeof(TIn) == 4 ? 2 : 3;
+}
+
 template <int DK, int DV, typename TIn, int MT, bool FUSED, int NT, bool MIX = false>
-__global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(3))) void verify_kernel(
+__global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(verify_waves_per_eu<TIn>()))) void verify_kernel(
     float *__restrict__ S, const TIn *__restrict__ q, const TIn *__restrict__ k,
     const TIn *__restrict__ v, const float *__restrict__ g, const float *__restrict__ beta,
     int T, int B, int H, float *__restrict__ o, uint8_t *__restrict__ rec, uint8_t *__restrict__ rprev,
