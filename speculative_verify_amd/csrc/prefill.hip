@@ -1225,7 +1225,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         vo_kq[u] = uint32_t(lane / (64 / RPB)) * kstride_b + 16u * uint32_t(kq_piece(NW * u + w));
     const uint32_t lk = lds_addr(sm.K), lq = lds_addr(sm.Q), lv = lds_addr(sm.V);
     const uint32_t vstride_b = uint32_t(vstride) * 2;
-    const uint32_t vo_v = uint32_t(lane >> 4) * vstride_b + 16u * uint32_t(lane & 15);   // V copies: row, piece
+    // V copies: lane l fills LDS slot l % 16 of row l / 16 of a 4-row block; rows
+    // keep their 16-byte pieces in the order slot = piece ^ 2 (row % 4), so the
+    // transposed reads of four consecutive rows hit different banks.
+    const uint32_t vo_v = uint32_t(lane >> 4) * vstride_b + 16u * uint32_t((lane & 15) ^ (2 * (lane >> 4)));
 
     // Per-lane LDS offsets of the P4 operands (aKQ, aM, aTR, set per chunk).  In
     // the tau order a result tile's token is t = T(tt) + tl, T(tt) = 32 (tt/2) +
@@ -1289,22 +1292,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 
 
         // P1: Gram tiles, transposed so that a lane holds four consecutive j of one
-        // t: wave w takes row band tt = w of A (from K K^T) and row band 3 - w of P
-        // (from Q K^T), all four tiles of each (the masks zero what lies above the
-        // diagonal), written as one 16-byte store of A[t][j .. j + 3] and two 8-byte
-        // stores of P's hi and lo parts per tile.
+        // t: wave w takes a row band of A (from K K^T) and one of P (from Q K^T),
+        // all four tiles of each (the masks zero what lies above the diagonal),
+        // written as one 16-byte store of A[t][j .. j + 3] and two 8-byte stores of
+        // P's hi and lo parts per tile.  The j side and P's band take rows in the
+        // tau order, which the key/query and matrix swizzles keep free of bank
+        // conflicts; A's band keeps rows 16 w .. 16 w + 15, for which its padded
+        // fp32 rows are conflict-free.
         {
-            const int ta = 16 * w + lr, tp = 16 * (3 - w) + lr;   // the lane's t in each band
+            const int ta = 16 * w + lr, tp = tau(3 - w, lr);   // the lane's t in each band
             f32x4 aT[4], pT[4];
 #pragma unroll
             for (int jt = 0; jt < 4; ++jt) aT[jt] = pT[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb2 = 0; kb2 < KB; ++kb2) {
                 const bf16x8 kt_b = lds16(sm.K + kq_off<DK>(ta, 4 * kb2 + lg));
-                const bf16x8 qt_b = lds16(sm.Q + kq_off<DK>(tp, 4 * kb2 + lg));
+                const bf16x8 qt_b = lds16(sm.Q + aKQ[kb2] + Tc(3 - w) * 2 * DK);
 #pragma unroll
                 for (int jt = 0; jt < 4; ++jt) {
-                    const bf16x8 kj = lds16(sm.K + kq_off<DK>(16 * jt + lr, 4 * kb2 + lg));
+                    const bf16x8 kj = lds16(sm.K + aKQ[kb2] + Tc(jt) * 2 * DK);
                     aT[jt] = mma(kj, kt_b, aT[jt]);
                     pT[jt] = mma(kj, qt_b, pT[jt]);
                 }
@@ -1312,7 +1318,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
             const float Gta = sm.G[ta], Gtp = sm.G[tp], bta = sm.bet[ta];
 #pragma unroll
             for (int jt = 0; jt < 4; ++jt) {
-                const int j0 = 16 * jt + 4 * lg;
+                const int j0 = Tc(jt) + 8 * lg;   // rows 4 lg + r of tile jt: tau(jt, 4 lg + r)
                 const float4 Gj = *reinterpret_cast<const float4 *>(&sm.G[j0]);
                 float av[4], pv[4];
 #pragma unroll
@@ -1378,7 +1384,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int blk = NW * u + w, row = 4 * blk + (ln >> 4);
-                dma16_nt(vbase + size_t(min(c0 + row, L - 1)) * vstride + 8 * (ln & 15), lv + blk * 1024);
+                dma16_nt(vbase + size_t(min(c0 + row, L - 1)) * vstride + 8 * ((ln & 15) ^ (2 * (ln >> 4))),
+                         lv + blk * 1024);
             }
         }
 
@@ -1458,7 +1465,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
                     const int t0 = 32 * p + 8 * lg + 4 * hh;
-                    vt[hh] = read_tr(sm.V + (t0 + (lr >> 2)) * 2 * DV + 2 * (32 * w + 16 * rt) + 8 * (lr & 3));
+                    const int vrow = t0 + (lr >> 2), vbyte = 2 * (32 * w + 16 * rt) + 8 * (lr & 3);
+                    vt[hh] = read_tr(sm.V + vrow * 2 * DV + ((((vbyte >> 4) ^ (2 * (vrow & 3))) << 4) | (vbyte & 15)));
                 }
                 float x[8];
 #pragma unroll
