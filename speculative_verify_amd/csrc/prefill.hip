@@ -1192,9 +1192,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     const int bh = blockIdx.x, b = bh / H, h = bh - b * H;
     const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // Value rows: lane column lr of row tile rt is row 32 w + 2 lr + rt, so a
+    // lane's two rows are adjacent (one 8-byte output store per token).
     int irow[2];
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) irow[rt] = 32 * w + 16 * rt + lr;
+    for (int rt = 0; rt < 2; ++rt) irow[rt] = 32 * w + 2 * lr + rt;
 
     // State: st[rt][kt][r] = S[irow[rt]][32 (kt/2) + 8 lg + 4 (kt%2) + r].
     float st[2][KT][4];
@@ -1226,9 +1228,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     const uint32_t lk = lds_addr(sm.K), lq = lds_addr(sm.Q), lv = lds_addr(sm.V);
     const uint32_t vstride_b = uint32_t(vstride) * 2;
     // V copies: lane l fills LDS slot l % 16 of row l / 16 of a 4-row block; rows
-    // keep their 16-byte pieces in the order slot = piece ^ 2 (row % 4), so the
-    // transposed reads of four consecutive rows hit different banks.
-    const uint32_t vo_v = uint32_t(lane >> 4) * vstride_b + 16u * uint32_t((lane & 15) ^ (2 * (lane >> 4)));
+    // keep their 16-byte pieces in the order slot = piece ^ vswz(row), vswz(row) =
+    // 4 ((row / 8) % 4), so the reads of rows 8 apart (one per lane group) hit
+    // different banks.  Block blk's rows share row / 8 = blk / 2.
+    auto vswz = [](int row) { return 4 * ((row >> 3) & 3); };
+    uint32_t vo_v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+        vo_v[u] = uint32_t(lane >> 4) * vstride_b + 16u * uint32_t((lane & 15) ^ vswz(4 * (NW * u + w)));
 
     // Per-lane LDS offsets of the P4 operands (aKQ, aM, aTR, set per chunk).  In
     // the tau order a result tile's token is t = T(tt) + tl, T(tt) = 32 (tt/2) +
@@ -1249,7 +1256,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         int ln = lane;
         asm volatile("" : "+v"(ln));
         const int lr = ln & 15, lg = ln >> 4;
-        const int irow[2] = {32 * w + lr, 32 * w + 16 + lr};
+        const int irow[2] = {32 * w + 2 * lr, 32 * w + 2 * lr + 1};
         const int tl = 8 * (lr >> 2) + (lr & 3), tal = 8 * lg + (lr >> 2);
         uint32_t aKQ[KB], aM[2], aTR[KT / 2];
 #pragma unroll
@@ -1378,13 +1385,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int blk = NW * u + w;
-                dma16s_nt(vc + size_t(4 * blk) * vstride_b, vo_v, lv + blk * 1024);
+                dma16s_nt(vc + size_t(4 * blk) * vstride_b, vo_v[u], lv + blk * 1024);
             }
         } else {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int blk = NW * u + w, row = 4 * blk + (ln >> 4);
-                dma16_nt(vbase + size_t(min(c0 + row, L - 1)) * vstride + 8 * ((ln & 15) ^ (2 * (ln >> 4))),
+                dma16_nt(vbase + size_t(min(c0 + row, L - 1)) * vstride + 8 * ((ln & 15) ^ vswz(row)),
                          lv + blk * 1024);
             }
         }
@@ -1458,23 +1465,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
                 ga[hh] = gate4(sm.gam, p, hh);
                 be[hh] = gate4(sm.bet, p, hh);
             }
+            // v[t][irow[0]] and v[t][irow[1]] (adjacent) by one 4-byte read per token.
+            float vv[2][2][4];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int vrow = 32 * p + 8 * lg + 4 * hh + r, vbyte = 2 * (32 * w + 2 * lr);
+                    const uint32_t pair = *reinterpret_cast<const uint32_t *>(
+                        sm.V + vrow * 2 * DV + ((((vbyte >> 4) ^ vswz(vrow)) << 4) | (vbyte & 15)));
+                    vv[0][hh][r] = __uint_as_float(pair << 16);
+                    vv[1][hh][r] = __uint_as_float(pair & 0xffff0000u);
+                }
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt) {
-                // v[t0 .. t0 + 3][irow[rt]] by one transposed read (V rows are 2 DV bytes).
-                bf16x4 vt[2];
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const int t0 = 32 * p + 8 * lg + 4 * hh;
-                    const int vrow = t0 + (lr >> 2), vbyte = 2 * (32 * w + 16 * rt) + 8 * (lr & 3);
-                    vt[hh] = read_tr(sm.V + vrow * 2 * DV + ((((vbyte >> 4) ^ (2 * (vrow & 3))) << 4) | (vbyte & 15)));
-                }
                 float x[8];
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        x[4 * hh + r] = (&be[hh].x)[r] * (static_cast<float>(vt[hh][r]) -
-                                                         (&ga[hh].x)[r] * X[rt][2 * p + hh][r]);
+                        x[4 * hh + r] = (&be[hh].x)[r] * (vv[rt][hh][r] - (&ga[hh].x)[r] * X[rt][2 * p + hh][r]);
                 rB[rt][p] = split8(x);
             }
         }
@@ -1527,9 +1537,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
                 for (int r = 0; r < 4; ++r) {
                     const int tr = 32 * (tt >> 1) + 8 * lg + 4 * (tt & 1) + r;
                     if (tr < n) {
-#pragma unroll
-                        for (int rt = 0; rt < 2; ++rt)
-                            __builtin_nontemporal_store(Ot[rt][r], orow + size_t(tr) * vstride + irow[rt]);
+                        typedef float f32x2 __attribute__((ext_vector_type(2)));
+                        __builtin_nontemporal_store(f32x2{Ot[0][r], Ot[1][r]},
+                                                    reinterpret_cast<f32x2 *>(orow + size_t(tr) * vstride + irow[0]));
                     }
                 }
             }
@@ -1583,7 +1593,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         const int lr = ln & 15, lg = ln >> 4;
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
-            float *Srow = S + (size_t(bh) * DV + 32 * w + 16 * rt + lr) * DK;
+            float *Srow = S + (size_t(bh) * DV + 32 * w + 2 * lr + rt) * DK;
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt)
                 *reinterpret_cast<float4 *>(Srow + 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1)) =
