@@ -175,30 +175,53 @@ __device__ inline void chunk_gates(SM &sm, float gt, float bt, int n, int lane) 
     sm.bet[lane] = bt;
 }
 
-// One 16x16 fp32 product on the fp32 MFMA, d + A B, with A(r, c) and B(r, c)
-// read through accessors: k-step s takes contraction index 4s + lg from lane
-// group lg.  The result is in the D layout: lane (lr, lg) holds rows 4lg .. 4lg + 3
-// of column lr.
-template <typename FA, typename FB>
-__device__ inline f32x4 mm16(FA a, FB b, f32x4 d, int lr, int lg) {
-    float av[4], bv[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        av[s] = a(lr, 4 * s + lg);
-        bv[s] = b(4 * s + lg, lr);
-    }
-#pragma unroll
-    for (int s = 0; s < 4; ++s) d = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s], bv[s], d, 0, 0, 0);
-    return d;
+// 16x16 fp32 operands of the inverse, by where they live.  RowMat: row-major
+// fp32 in LDS, element (r, c) at p[r * ld + c] (16-byte aligned rows and
+// column bases).  ColMat: a wave's scratch matrix, stored transposed, element
+// (r, c) at p[20 c + r].
+struct RowMat {
+    const float *p;
+    int ld;
+};
+struct ColMat {
+    const float *p;
+};
+
+// The four values a lane contributes over the four k-steps of a product: k-step
+// s takes contraction index 4 lg + s from lane group lg, so a lane's A values
+// are A(lr, 4 lg .. 4 lg + 3) and its B values B(4 lg .. 4 lg + 3, lr); where
+// those are consecutive in memory (A row-major, B stored transposed) they come
+// in one 16-byte read.
+__device__ inline float4 a_vals(const RowMat &m, int lr, int lg) {
+    return *reinterpret_cast<const float4 *>(m.p + lr * m.ld + 4 * lg);
+}
+__device__ inline float4 a_vals(const ColMat &m, int lr, int lg) {
+    return make_float4(m.p[20 * (4 * lg) + lr], m.p[20 * (4 * lg + 1) + lr], m.p[20 * (4 * lg + 2) + lr],
+                       m.p[20 * (4 * lg + 3) + lr]);
+}
+__device__ inline float4 b_vals(const RowMat &m, int lr, int lg) {
+    return make_float4(m.p[(4 * lg) * m.ld + lr], m.p[(4 * lg + 1) * m.ld + lr], m.p[(4 * lg + 2) * m.ld + lr],
+                       m.p[(4 * lg + 3) * m.ld + lr]);
+}
+__device__ inline float4 b_vals(const ColMat &m, int lr, int lg) {
+    return *reinterpret_cast<const float4 *>(m.p + 20 * lr + 4 * lg);
+}
+
+// One 16x16 fp32 product on the fp32 MFMA, d + A B.  The result is in the D
+// layout: lane (lr, lg) holds rows 4lg .. 4lg + 3 of column lr.
+template <typename MA, typename MB>
+__device__ inline f32x4 mm16(const MA &a, const MB &b, f32x4 d, int lr, int lg) {
+    const float4 av = a_vals(a, lr, lg), bv = b_vals(b, lr, lg);
+    d = __builtin_amdgcn_mfma_f32_16x16x4f32(av.x, bv.x, d, 0, 0, 0);
+    d = __builtin_amdgcn_mfma_f32_16x16x4f32(av.y, bv.y, d, 0, 0, 0);
+    d = __builtin_amdgcn_mfma_f32_16x16x4f32(av.z, bv.z, d, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(av.w, bv.w, d, 0, 0, 0);
 }
 
 // A D-layout tile into a wave's scratch matrix, stored transposed (column c at
-// 20 c): one 16-byte write per lane; read back through scr_at.
+// 20 c): one 16-byte write per lane; read back as a ColMat.
 __device__ inline void scr_put(float *m, const f32x4 &d, int lr, int lg) {
     *reinterpret_cast<float4 *>(m + 20 * lr + 4 * lg) = make_float4(d[0], d[1], d[2], d[3]);
-}
-__device__ inline auto scr_at(const float *m) {
-    return [m](int r, int c) { return m[20 * c + r]; };
 }
 
 // Linv = (I + A)^{-1} for the chunk's strictly lower A (fp32 [C][C + 4] in LDS)
@@ -212,45 +235,47 @@ __device__ inline auto scr_at(const float *m) {
 // inverses X_A, X_B of the two 32x32 diagonal blocks, and the lower-left 32x32
 // block is -X_B A_BA X_A.
 // Every product of lower-triangular factors keeps exact zeros above the
-// diagonal and ones on it, so the diagonal blocks need no masking.
+// diagonal and ones on it, so the diagonal blocks need no masking.  Tm may be
+// Am itself: each block is read before it is overwritten.
 template <typename MA, typename MT, typename Side>
 __device__ inline void tri_inverse(const MA &Am, MT &Tm, float *scr, int w, int lane, Side &&side) {
     const int lr = lane & 15, lg = lane >> 4;
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    constexpr int LD = C + 4;
+    const auto A = [&](int bi, int bj) { return RowMat{&Am[16 * bi][16 * bj], LD}; };
+    const auto X = [&](int bi, int bj) { return RowMat{&Tm[16 * bi][16 * bj], LD}; };
     if (w >= 4) side();   // waves past the fourth: independent work, if any
     if (w < 4) {
         const int b0 = 16 * w;
         float *s0 = scr + w * 640, *s1 = s0 + 320;
-        const auto N = [&](int r, int c) { return Am[b0 + r][b0 + c]; };
-        const f32x4 p1 = mm16(N, N, z, lr, lg);               // N^2
+        const RowMat N = A(w, w);
+        const f32x4 p1 = mm16(N, N, z, lr, lg);                       // N^2
         scr_put(s0, p1, lr, lg);
-        const f32x4 p2 = mm16(scr_at(s0), scr_at(s0), z, lr, lg);   // N^4
-        const f32x4 y = mm16(N, scr_at(s0), z, lr, lg);       // N^3
-        f32x4 x;                                               // (I - N)(I + N^2)
+        const f32x4 p2 = mm16(ColMat{s0}, ColMat{s0}, z, lr, lg);     // N^4
+        const f32x4 y = mm16(N, ColMat{s0}, z, lr, lg);               // N^3
+        f32x4 x;                                                       // (I - N)(I + N^2)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = 4 * lg + r;
             x[r] = (row == lr ? 1.f : 0.f) - Am[b0 + row][b0 + lr] + p1[r] - y[r];
         }
-        scr_put(s0, p2, lr, lg);                               // (this wave's reads of N^2 came first)
+        scr_put(s0, p2, lr, lg);                                       // (this wave's reads of N^2 came first)
         scr_put(s1, x, lr, lg);
-        const f32x4 p3 = mm16(scr_at(s0), scr_at(s0), z, lr, lg);   // N^8
-        x = mm16(scr_at(s1), scr_at(s0), x, lr, lg);           // X (I + N^4)
+        const f32x4 p3 = mm16(ColMat{s0}, ColMat{s0}, z, lr, lg);     // N^8
+        x = mm16(ColMat{s1}, ColMat{s0}, x, lr, lg);                  // X (I + N^4)
         scr_put(s0, p3, lr, lg);
         scr_put(s1, x, lr, lg);
-        x = mm16(scr_at(s1), scr_at(s0), x, lr, lg);           // X (I + N^8)
+        x = mm16(ColMat{s1}, ColMat{s0}, x, lr, lg);                  // X (I + N^8)
 #pragma unroll
         for (int r = 0; r < 4; ++r) Tm[b0 + 4 * lg + r][b0 + lr] = x[r];
     }
     __syncthreads();
-    const auto A = [&](int bi, int bj) { return [&Am, bi, bj](int r, int c) { return Am[16 * bi + r][16 * bj + c]; }; };
-    const auto X = [&](int bi, int bj) { return [&Tm, bi, bj](int r, int c) { return Tm[16 * bi + r][16 * bj + c]; }; };
     // The off-diagonal block inside each 32x32 diagonal block: X_10 and X_32.
     if (w < 2) {
         const int j = 2 * w, i = j + 1;
         float *s0 = scr + w * 640;
         scr_put(s0, mm16(A(i, j), X(j, j), z, lr, lg), lr, lg);
-        const f32x4 x = mm16(X(i, i), scr_at(s0), z, lr, lg);
+        const f32x4 x = mm16(X(i, i), ColMat{s0}, z, lr, lg);
 #pragma unroll
         for (int r = 0; r < 4; ++r) Tm[16 * i + 4 * lg + r][16 * j + lr] = -x[r];
     }
@@ -268,8 +293,8 @@ __device__ inline void tri_inverse(const MA &Am, MT &Tm, float *scr, int w, int 
     // ... then X_ij = -sum_{m=2}^{i} X_im Y_mj, block (i, j) on wave 2 (i - 2) + j.
     if (w < 4) {
         const int i = 2 + (w >> 1), j = w & 1;
-        f32x4 x = mm16(X(i, 2), scr_at(scr + j * 640), z, lr, lg);
-        if (i == 3) x = mm16(X(3, 3), scr_at(scr + (2 + j) * 640), x, lr, lg);
+        f32x4 x = mm16(X(i, 2), ColMat{scr + j * 640}, z, lr, lg);
+        if (i == 3) x = mm16(X(3, 3), ColMat{scr + (2 + j) * 640}, x, lr, lg);
 #pragma unroll
         for (int r = 0; r < 4; ++r) Tm[16 * i + 4 * lg + r][16 * j + lr] = -x[r];
     }
