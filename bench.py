@@ -679,7 +679,7 @@ def summarize_profiles(args):
             com, [commit_bytes(LAYERS, HEADS, DK, DV, com_n[i], es) for i in range(len(com))])
     # Prefill: every call launches either prefill_kernel, or one prep launch and
     # one stage launch per chunk segment; per call.
-    pk = kernel_rows("prefill_kernel<")
+    pk = kernel_rows("prefill_kernel<") + kernel_rows("prefill_pass_kernel<")
     pp = kernel_rows("prefill_prep_kernel")
     ps = kernel_rows("prefill_stage_kernel")
     calls = len(pp) if pp else len(pk)
@@ -726,7 +726,7 @@ def summarize_mfma(d, commands, src_hash):
     out = {"sources_sha256_16": src_hash, "command": next((c for c in commands if "--pmc SQ_INSTS_VALU_MFMA" in c), None),
            "durations_from": "plain benchmark run" if timed_by == "bench.json" else "the counter run", "legs": {}}
     for leg, tags in (("prefill", ("prefill_prep_kernel", "prefill_stage_kernel")),
-                      ("prefill_long", ("prefill_kernel<",))):
+                      ("prefill_long", ("prefill_pass_kernel<", "prefill_kernel<"))):
         ds = [e for e in disp.values() if any(t in e["name"] for t in tags)]
         b = bench_out.get(leg, {})
         if not ds or "avg_launch_us" not in b:
