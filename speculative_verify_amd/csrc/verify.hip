@@ -53,16 +53,53 @@ __device__ inline int xoff(int x, int piece) {  // byte offset of piece `piece` 
     return x * (2 * DK) + ((piece ^ xswz<DK>(x)) << 4);
 }
 
-// A operand row x of the bf16 X for key block p: keys 16(2p) + 4lg + {0..3} in
-// slots 0..3 and 16(2p+1) + 4lg + {0..3} in slots 4..7 (the keys a lane holds in
-// its state registers for that block).
+// A operand row x of the bf16 X for key block p: keys 32p + 8lg .. 32p + 8lg + 7,
+// one 16-byte piece (the keys a lane holds in its state registers for that block).
 template <int DK>
 __device__ inline bf16x8 xrow_bf16(const uint8_t *Xb, int x, int p, int lg) {
-    const int h8 = (lg & 1) << 3;
-    const bf16x4 lo4 = *reinterpret_cast<const bf16x4 *>(Xb + xoff<DK>(x, 4 * p + (lg >> 1)) + h8);
-    const bf16x4 hi4 = *reinterpret_cast<const bf16x4 *>(Xb + xoff<DK>(x, 4 * p + 2 + (lg >> 1)) + h8);
-    return __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+    return *reinterpret_cast<const bf16x8 *>(Xb + xoff<DK>(x, 4 * p + lg));
 }
+
+// The state's lane layout.  In registers, lane (lr, lg) of a wave holds row lr of
+// a 16-row tile at keys 32c + 8lg + {0..7} for each 32-key block c (float4 2c and
+// 2c + 1): the B-operand layout of the bf16 MFMA, c being the contraction block.
+// In memory, a copy instruction covers 8 rows x 128 bytes: copy (rg, c) of lane l
+// is row 8rg + (l & 7), bytes 128c + 16(l >> 3) of the row.  Whole 128-byte lines
+// per instruction stream at the copy rate; the 16 rows x 64 bytes that the
+// register layout would read directly reached only about three quarters of it on
+// the same in-place stream (both measured).  Lane l holds its own row in copy rg
+// = (l & 15) / 8 and the row of lane l ^ 8 in the other, at the key quad that lane
+// needs: one DPP move (row_ror:8 with a bank mask) per register puts every quad
+// in place, and the inverse moves restore the copy layout before a store.
+constexpr int kRor8 = 0x128;   // DPP row_ror:8 (lane l reads lane l ^ 8 of its row)
+__device__ inline float dpp_ror8(float old, float src, int bank_mask_hi) {
+    // bank_mask_hi: lanes 8..15 of each row (true) or lanes 0..7 (false) take src.
+    return bank_mask_hi
+               ? __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src), kRor8, 0xf, 0xc, false))
+               : __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src), kRor8, 0xf, 0x3, false));
+}
+// Copy layout (a = copy rg 0, c = copy rg 1 of one 128-byte block) <-> register
+// layout (keys + 0..3, keys + 4..7), in place.
+// Both directions are the same exchange: lanes 8..15 of a row take the first
+// register from the second of lane l ^ 8, lanes 0..7 the second from the first.
+__device__ inline void swap_quads(float &a, float &c) {
+    const float t = a;
+    a = dpp_ror8(a, c, true);
+    c = dpp_ror8(c, t, false);
+}
+__device__ inline void swap_quads(float4 &a, float4 &c) {
+    swap_quads(a.x, c.x);
+    swap_quads(a.y, c.y);
+    swap_quads(a.z, c.z);
+    swap_quads(a.w, c.w);
+}
+// Raw buffer accesses: the descriptor's fourth word for gfx9-family targets, and
+// the cache-policy bit of a streaming (non-temporal) access.
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kBufferNt = 2;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// Key of component e of state register m of lane group lg (KM registers a row).
+__device__ inline int skey(int m, int lg) { return 32 * (m >> 1) + 8 * lg + 4 * (m & 1); }
 
 // The GDN mixer around the recurrence (MIX): the kernel builds q, k, v and the
 // gates itself from the layer's raw in-projection rows, and applies the gated
@@ -377,19 +414,41 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(verify_waves
     // Compiler-only barrier: keep the loads above ahead of the state loads, so
     // consuming them never waits for the state.
     asm volatile("" ::: "memory");
-    // 3. The wave's state rows 64w + 16nt + lr, keys 16m + 4lg .. +3, tile by tile.
+    // 3. The wave's state rows, 16-row tile by tile (tile nt: rows RW w + 16nt ..,
+    //    copies in the whole-line layout, put into the register layout before use).
     //    The plain verify issues all four tiles at once; the fused kernel keeps two
     //    tiles in flight and issues the next after writing one back, so that its
     //    reads and write-backs share the memory system instead of queueing as a
     //    read phase followed by a write phase.
     constexpr int NPRE = (FUSED || MIX) ? (NT < 2 ? NT : 2) : NT;   // tiles loaded up front
     constexpr int NEARLY = FUSED ? (NPRE < 1 ? NPRE : 1) : 0;          // tiles committed before the Gram
-    const float *Sw = S + (size_t(bh) * DV + rbase + RW * w + lr) * DK + 4 * lg;
+    // The copies go through a buffer descriptor over the wave's RW rows (in scalar
+    // registers): lane l's byte offset (row l & 7 of the tile, 16 bytes l >> 3 of a
+    // line) in one register and the copy's constant offset in a scalar one, where
+    // 64-bit lane addresses would take two registers per copy.
+    const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+        S + (size_t(bh) * DV + rbase + RW * w) * DK, 0, RW * DK * 4, kBufferWord3);
+    const uint32_t soff = uint32_t(((lane & 7) * DK + 4 * (lane >> 3)) * 4);
+    auto scopy = [](int nt, int rg, int c) { return uint32_t(((16 * nt + 8 * rg) * DK + 32 * c) * 4); };
     float4 sreg[NT][KM];
     auto load_tile = [&](int nt) {
 #pragma unroll
-        for (int m = 0; m < KM; ++m)
-            sreg[nt][m] = ld_stream(Sw + size_t(16 * nt) * DK + 16 * m);
+        for (int c = 0; c < KM / 2; ++c)
+#pragma unroll
+            for (int rg = 0; rg < 2; ++rg)
+                sreg[nt][2 * c + rg] = __builtin_bit_cast(
+                    float4, __builtin_amdgcn_raw_buffer_load_b128(srs, soff, scopy(nt, rg, c), kBufferNt));
+    };
+    auto store_copy = [&](int nt, int rg, int c, const float4 &val) {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, val), srs, soff, scopy(nt, rg, c), kBufferNt);
+    };
+    // The tile's registers into the register layout, once they have landed.
+    auto fix_tile = [&](int nt) {
+#pragma unroll
+        for (int c = 0; c < KM / 2; ++c) {
+            swap_quads(sreg[nt][2 * c], sreg[nt][2 * c + 1]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     };
 #pragma unroll
     for (int nt = 0; nt < NPRE; ++nt) load_tile(nt);
@@ -492,14 +551,56 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(verify_waves
             }
         }
     }
+    // [K;Q] S^T of state tile nt (register layout) into P.  bf16 inputs: the fp32
+    // state is split into bf16 high and low parts against the exact bf16 X (two
+    // bf16 MFMAs per 32 keys); fp32 inputs: fp32 MFMA.  The contraction slots visit
+    // the same keys in A and B.
+    auto products = [&](int nt) {
+        f32x4 acc[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (kBf16) {
+#pragma unroll
+            for (int p = 0; p < KM / 2; ++p) {
+                bf16x8 shi, slo;
+                split_bf16(sreg[nt][2 * p], sreg[nt][2 * p + 1], shi, slo);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    const bf16x8 a = xrow_bf16<DK>(Xb, 16 * mt + lr, p, lg);
+                    acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, shi, acc[mt], 0, 0, 0);
+                    acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, slo, acc[mt], 0, 0, 0);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int m = 0; m < KM; ++m) {
+                float4 a[MT];
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    a[mt] = *reinterpret_cast<const float4 *>(X + (16 * mt + lr) * XS + skey(m, lg));
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt)
+                        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(comp(a[mt], c), comp(sreg[nt][m], c),
+                                                                       acc[mt], 0, 0, 0);
+            }
+        }
+        // Lane (lr, lg) of a 16x16 result tile holds rows 4lg..4lg+3 of column lr.
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) P[16 * mt + 4 * lg + r][RW * w + 16 * nt + lr] = acc[mt][r];
+    };
     // FUSED: the commit of state tile nt (in registers), its write-back, and the
     // load of the tile NPRE ahead.  Needs only the pending block's rows, so the
     // first NEARLY tiles are committed before this block's Gram matrix and
     // coefficients, and the state keeps streaming meanwhile.
     auto commit_tile = [&](int nt) {
+        fix_tile(nt);
         if (cn > 0) {
             // S_n = exp(G_n) S + sum_{j < n} exp(G_n - G_j) delta_j k_j^T for this
-            // tile (row 64w + 16nt + lr, keys 16m + 4lg + {0..3}), written back.
+            // tile (row RW w + 16nt + lr, keys skey(m, lg) + {0..3}), written back.
             const int row = rbase + RW * w + 16 * nt + lr;
 #pragma unroll
             for (int m = 0; m < KM; ++m) {
@@ -519,16 +620,27 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(verify_waves
             };
             const int nr = min(cn, CR);
             if (esp == 2) {
+                // bf16 keys: a lane's 8 keys of block c are consecutive, one 16-byte
+                // read, unpacked at the update.
 #pragma unroll 1
                 for (int j = 0; j < nr; ++j) {
-                    float4 kv[KM];
+                    uint4 kr[KM / 2];
 #pragma unroll
-                    for (int m = 0; m < KM; ++m) {
-                        const uint2 r2 = *reinterpret_cast<const uint2 *>(kraw + (j * DK + 16 * m + 4 * lg) * 2);
-                        kv[m] = make_float4(__uint_as_float(r2.x << 16), __uint_as_float(r2.x & 0xffff0000u),
-                                            __uint_as_float(r2.y << 16), __uint_as_float(r2.y & 0xffff0000u));
+                    for (int c = 0; c < KM / 2; ++c)
+                        kr[c] = *reinterpret_cast<const uint4 *>(kraw + (j * DK + skey(2 * c, lg)) * 2);
+                    const float cj = cdraw[j * DV + row];
+#pragma unroll
+                    for (int c = 0; c < KM / 2; ++c) {
+                        float4 &lo = sreg[nt][2 * c], &hi = sreg[nt][2 * c + 1];
+                        lo.x += cj * __uint_as_float(kr[c].x << 16);
+                        lo.y += cj * __uint_as_float(kr[c].x & 0xffff0000u);
+                        lo.z += cj * __uint_as_float(kr[c].y << 16);
+                        lo.w += cj * __uint_as_float(kr[c].y & 0xffff0000u);
+                        hi.x += cj * __uint_as_float(kr[c].z << 16);
+                        hi.y += cj * __uint_as_float(kr[c].z & 0xffff0000u);
+                        hi.z += cj * __uint_as_float(kr[c].w << 16);
+                        hi.w += cj * __uint_as_float(kr[c].w & 0xffff0000u);
                     }
-                    add_row(cdraw[j * DV + row], kv);
                 }
             } else {
 #pragma unroll 1
@@ -536,7 +648,7 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(verify_waves
                     float4 kv[KM];
 #pragma unroll
                     for (int m = 0; m < KM; ++m)
-                        kv[m] = *reinterpret_cast<const float4 *>(kraw + (j * DK + 16 * m + 4 * lg) * 4);
+                        kv[m] = *reinterpret_cast<const float4 *>(kraw + (j * DK + skey(m, lg)) * 4);
                     add_row(cdraw[j * DV + row], kv);
                 }
             }
@@ -549,7 +661,7 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(verify_waves
                 float4 kv[KM];
 #pragma unroll
                 for (int m = 0; m < KM; ++m) {
-                    const int key = 16 * m + 4 * lg;
+                    const int key = skey(m, lg);
                     if (esp == 2) {
                         const uint2 r2 = *reinterpret_cast<const uint2 *>(rprev + RLp.kcopy + (rj * DK + key) * 2);
                         kv[m] = make_float4(__uint_as_float(r2.x << 16), __uint_as_float(r2.x & 0xffff0000u),
@@ -560,9 +672,15 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(verify_waves
                 }
                 add_row(c, kv);
             }
-            float *Sw_out = S + (size_t(bh) * DV + row) * DK + 4 * lg;
+            // Stored in the copy layout: swapped, stored and swapped back in place.
 #pragma unroll
-            for (int m = 0; m < KM; ++m) st_stream(Sw_out + 16 * m, sreg[nt][m]);
+            for (int c = 0; c < KM / 2; ++c) {
+                swap_quads(sreg[nt][2 * c], sreg[nt][2 * c + 1]);
+                store_copy(nt, 0, c, sreg[nt][2 * c]);
+                store_copy(nt, 1, c, sreg[nt][2 * c + 1]);
+                swap_quads(sreg[nt][2 * c], sreg[nt][2 * c + 1]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
         if (nt + NPRE < NT) load_tile(nt + NPRE);
     };
@@ -599,8 +717,8 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(verify_waves
 
     // Gram matrix X X^T, each wave over its share of the keys, while the state is
     // still arriving: exact on bf16 MFMA for bf16 rows, fp32 MFMA otherwise.
-    // Contraction slots visit keys 16(2p) + 4lg + {0..3} and 16(2p+1) + 4lg +
-    // {0..3} (bf16), or 16m + 4lg + c (fp32), in A and B alike.
+    // Contraction slots visit keys 32p + 8lg + {0..7} (bf16), or 16m + 4lg + c
+    // (fp32), in A and B alike.
     {
         f32x4 gacc[MT][MT];
 #pragma unroll
@@ -664,52 +782,18 @@ __global__ __launch_bounds__(DV) __attribute__((amdgpu_waves_per_eu(verify_waves
     }
     __syncthreads();
 
-    // [K;Q] S^T, tile by tile as the state arrives.  bf16 inputs: the fp32 state
-    // is split into bf16 high and low parts against the exact bf16 X (two bf16
-    // MFMAs per 32 keys); fp32 inputs: fp32 MFMA.  The contraction slots visit the
-    // same keys in A and B.
+    // The products tile by tile as the state arrives.
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         if constexpr (FUSED) {
             if (nt >= NEARLY) commit_tile(nt);
-        } else if constexpr (MIX) {
-            if (nt + NPRE < NT) load_tile(nt + NPRE);
-        }
-        f32x4 acc[MT];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if constexpr (kBf16) {
-#pragma unroll
-            for (int p = 0; p < KM / 2; ++p) {
-                bf16x8 shi, slo;
-                split_bf16(sreg[nt][2 * p], sreg[nt][2 * p + 1], shi, slo);
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    const bf16x8 a = xrow_bf16<DK>(Xb, 16 * mt + lr, p, lg);
-                    acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, shi, acc[mt], 0, 0, 0);
-                    acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, slo, acc[mt], 0, 0, 0);
-                }
-            }
         } else {
-#pragma unroll
-            for (int m = 0; m < KM; ++m) {
-                float4 a[MT];
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-                    a[mt] = *reinterpret_cast<const float4 *>(X + (16 * mt + lr) * XS + 16 * m + 4 * lg);
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-#pragma unroll
-                    for (int mt = 0; mt < MT; ++mt)
-                        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(comp(a[mt], c), comp(sreg[nt][m], c),
-                                                                       acc[mt], 0, 0, 0);
+            fix_tile(nt);
+            if constexpr (MIX) {
+                if (nt + NPRE < NT) load_tile(nt + NPRE);
             }
         }
-        // Lane (lr, lg) of a 16x16 result tile holds rows 4lg..4lg+3 of column lr.
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) P[16 * mt + 4 * lg + r][RW * w + 16 * nt + lr] = acc[mt][r];
+        products(nt);
     }
     // P columns RW w .. RW w + RW - 1 are this wave's own; its LDS operations
     // complete in order, and the compiler-only barrier keeps the compiler from
