@@ -739,18 +739,19 @@ __device__ inline bf16x8 lds16(const uint8_t *p) { return *reinterpret_cast<cons
 // workgroup's 32) and keys 64 kh .. 64 kh + 63 of their state; of the output
 // tiles it finalises tt = kh and kh + 2, i.e. tokens 32p + 8a + 4kh + r.
 
-// Store the wave's finished outputs of one chunk (its 32 tokens x 16 value
-// columns) from the staging buffer as 64-byte row segments (tokens < n).  obase
-// points at o for the chunk's first token and the workgroup's first value
+// Store a chunk's finished outputs (64 tokens x the workgroup's 32 value
+// columns, every wave's, after a barrier) from the staging buffer: wave w takes
+// tokens 16w .. 16w + 15 as whole 128-byte rows, 8 a store (tokens < n).  Whole
+// lines: half-line streaming stores of the same bytes drain markedly slower.
+// obase points at o for the chunk's first token and the workgroup's first value
 // column; ostride is one token.
 template <int DK>
-__device__ inline void scan_store_o(const ScanLds<DK> &sm, int n, int lane, int g, int kh,
+__device__ inline void scan_store_o(const ScanLds<DK> &sm, int n, int lane, int w,
                                     float *__restrict__ obase, size_t ostride) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-        const int j = 16 * i + (lane >> 2);                    // token index among the wave's 32
-        const int row = 32 * (j >> 4) + 8 * ((j >> 2) & 3) + 4 * kh + (j & 3);
-        const int col = 16 * g + 4 * (lane & 3);
+        const int row = 16 * w + 8 * i + (lane >> 3);
+        const int col = 4 * (lane & 7);
         const float4 v4 = *reinterpret_cast<const float4 *>(&sm.O[row * kOStride + col]);
         if (row < n) st_stream(obase + size_t(row) * ostride + col, v4);
     }
@@ -1089,7 +1090,7 @@ __device__ __forceinline__ void scan_role(ScanLds<DK> &sm, int wg, int nscan, fl
         __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) expcnt(7) lgkmcnt(0)
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        if (c > cbeg) scan_store_o<DK>(sm, C, lane, g, kh, ob + size_t(c0 - C) * ostride, ostride);
+        if (c > cbeg) scan_store_o<DK>(sm, C, lane, w, ob + size_t(c0 - C) * ostride, ostride);
         if (c + 1 < cend) issue(c + 1);
         asm volatile("" ::: "memory");
         if (kh)
@@ -1102,8 +1103,9 @@ __device__ __forceinline__ void scan_role(ScanLds<DK> &sm, int wg, int nscan, fl
         step(c, IntC<0>{});
         if (c + 1 < cend) step(c + 1, IntC<1>{});
     }
-    asm volatile("" ::: "memory");
-    scan_store_o<DK>(sm, min(C, L - (cend - 1) * C), lane, g, kh, ob + size_t(cend - 1) * C * ostride, ostride);
+    // The last chunk's outputs, once every wave has staged its part.
+    __syncthreads();
+    scan_store_o<DK>(sm, min(C, L - (cend - 1) * C), lane, w, ob + size_t(cend - 1) * C * ostride, ostride);
 
 #pragma unroll
     for (int kt = 0; kt < KTH; ++kt) {
